@@ -1,0 +1,34 @@
+"""Build the CPU oracle shared library (test infrastructure only).
+
+    python oracle/build.py [--out PATH] [--src PATH]
+
+gcc, C99, no floating-point contraction and no fast-math, so every fp32
+rounding is the one the source writes; OpenMP spreads independent queries.
+"""
+import argparse
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "qsa_oracle.c")
+LIB = os.path.join(HERE, "libqsa_oracle.so")
+FLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+         "-shared", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(out: str = LIB, src: str = SRC, extra=()) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", *FLAGS, *extra, src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=LIB)
+    ap.add_argument("--src", default=SRC)
+    a = ap.parse_args()
+    print(build(a.out, a.src))
+    sys.exit(0)

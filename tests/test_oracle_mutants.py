@@ -1,0 +1,88 @@
+"""Test power of the oracle pins: plant one mistake at a time in the oracle
+source (on the CPU), rebuild it, and require that some pin fails.
+
+The battery imitates the mutation record of the LocalAI QSA-block commit
+(section "The battery"): every mutant is proved applied (its edit must match
+exactly once), every build's return code is checked before any pin runs, and
+no mutant may survive.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as ob
+import oracle_pins
+
+SRC = ob.SRC
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+MUTANTS = {
+    "pool_divisor": ("pooled[j * d_idx + x] = acc / (float)r;",
+                     "pooled[j * d_idx + x] = acc / (float)(r - 1);"),
+    "pool_drops_first_token": ("for (int32_t s = 0; s < r; ++s) acc",
+                               "for (int32_t s = 1; s < r; ++s) acc"),
+    "score_no_relu": ("a = (a > 0.0f) ? a : 0.0f;", "a = (a > 0.0f) ? a : a;"),
+    "score_no_scale": ("float a = c * d;", "float a = d;"),
+    "score_weight_index": ("s = fmaf(w[h], a, s);", "s = fmaf(w[0], a, s);"),
+    "score_wrong_head_query": ("const float* qh = qI + (int64_t)h * d_idx;",
+                               "const float* qh = qI + (int64_t)0 * d_idx;"),
+    "score_transposed_pooled": ("const float* kb = pooled + j * d_idx;",
+                                "const float* kb = pooled + j;"),
+    "topk_tiebreak_highest": ("return (a->j < b->j) ? -1 : (a->j > b->j);",
+                              "return (a->j > b->j) ? -1 : (a->j < b->j);"),
+    "topk_bottom_k": ("if (a->s > b->s) return -1;", "if (a->s < b->s) return -1;"),
+    "topk_skips_best": ("sel[i] = all[i].j;", "sel[i] = all[i + 1].j;"),
+    "candidates_short_by_one": ("const int64_t nb = n / r;", "const int64_t nb = (n - 1) / r;"),
+    "tail_dropped_last": ("for (int64_t t = nb * r; t < n; ++t) tokens[c++] = t;",
+                          "for (int64_t t = nb * r; t < n - 1; ++t) tokens[c++] = t;"),
+    "tail_reads_future": ("int64_t n = p + 1, c = 0;", "int64_t n = p + 2, c = 0;"),
+    "gqa_map_modulo": ("int32_t kvh = h / g;", "int32_t kvh = h % Hkv;"),
+    "gate_silu": ("double gt = 1.0 / (1.0 + exp(-(double)gate[(int64_t)h * D + x]));",
+                  "double gt = (double)gate[(int64_t)h * D + x] / (1.0 + exp(-(double)gate[(int64_t)h * D + x]));"),
+    "attn_no_scale": ("z[i] = scale * acc;", "z[i] = acc;"),
+    "pv_reads_keys": ("const float* vr = V + (tokens[i] * Hkv + kvh) * D;",
+                      "const float* vr = K + (tokens[i] * Hkv + kvh) * D;"),
+    "dense_layer_drops_self": ("for (int64_t t = 0; t < n; ++t) tokens[c++] = t;",
+                               "for (int64_t t = 0; t + 1 < n; ++t) tokens[c++] = t;"),
+}
+
+
+def test_every_mutant_is_distinct_and_applies():
+    text = open(SRC).read()
+    for name, (a, b) in MUTANTS.items():
+        assert text.count(a) == 1, name
+        assert a != b, name
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_killed(name, tmp_path):
+    a, b = MUTANTS[name]
+    text = open(SRC).read()
+    assert text.count(a) == 1
+    src = tmp_path / "mut.c"
+    src.write_text(text.replace(a, b))
+    lib = str(tmp_path / "libmut.so")
+    ob.build(lib, str(src))                 # raises if the build fails
+    assert os.path.exists(lib)
+    # Each mutant runs in a child process: a mutant that corrupts memory and
+    # aborts is killed too, and cannot take the test session down with it.
+    code = (
+        "import sys, oracle, oracle_pins\n"
+        f"m = oracle.load({lib!r})\n"
+        "failed = []\n"
+        "for pin in oracle_pins.ALL_PINS:\n"
+        "    try:\n"
+        "        pin(m)\n"
+        "    except (AssertionError, ValueError):\n"
+        "        failed.append(pin.__name__)\n"
+        "print('FAILED_PINS', failed)\n"
+        "sys.exit(1 if failed else 0)\n")
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([ROOT, HERE, env.get("PYTHONPATH", "")])
+    env["OMP_NUM_THREADS"] = "2"
+    proc = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                          text=True, timeout=300)
+    assert proc.returncode != 0, f"mutant {name} survived every pin"
