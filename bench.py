@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA hot path on one MI355X.
+
+A step is one QSA layer step for one batch: append the new tokens' K/V and
+indexer keys, pool completed blocks, score, select, and attend
+(``qsa_forward``).  The default workload is the ragged batched decode at up
+to 128K context (32 sequences, contexts ~U[8192, 131072], paged KV), the
+configuration the decode tok/s + HBM GB/s metric is quoted on.
+
+Cache memory (256 MB on MI355X) would hold one step's selected KV, so the
+steps rotate over several layer copies of the caches (distinct buffers, as
+the QSA layers of a model are) and every step's bytes come from HBM.
+
+Printed: ONE JSON line with the throughput, a roofline object for the
+dominant kernel (the attention kernel: its algorithmic bytes per launch over
+its average launch time, measured with HIP events on the launch stream) and
+the CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA decode tok/s + HBM GB/s at 128K ctx; prefill TFLOP/s (selected blocks)"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ragged_paged_decode_128k_bf16")
+    ap.add_argument("--layers", type=int, default=0, help="cache copies to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the QSA hot path "
+                                   "has no multi-GPU leg (see DESIGN.md, sharding)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_keys_amd import qsa, runner, workloads
+
+    qsa.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    sp = workloads.SPECS[name]
+    if sp.kind != "decode":
+        print(json.dumps({"error": "bench.py times the decode workloads; prefill is measured by "
+                                   "the parity runs", "workload": name}))
+        sys.exit(2)
+
+    t0 = time.time()
+    case = workloads.make_case(name, seed=0)
+    log(f"[bench] workload {name}: drawn in {time.time() - t0:.1f}s, ctx "
+        f"min/max {min(case.ctx)}/{max(case.ctx)}")
+
+    B, r, k = sp.n_seqs, sp.block_size, sp.k_blocks
+    Hq, Hkv, D, HI, dI = sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads, sp.idx_dim
+    esz = 2  # bf16
+
+    # Algorithmic bytes of one step (host formula from positions only).
+    def step_bytes(ctx_now):
+        kv = idx = 0
+        for c in ctx_now:
+            n = c + 1
+            nb = n // r
+            nsel = r * min(k, nb) + (n - r * nb)
+            kv += nsel * Hkv * D * esz * 2
+            idx += nb * dI * 4                      # pooled keys read by the scorer
+        qgo = B * Hq * D * esz * 3 + B * (HI * dI * esz + HI * 4)
+        new_rows = B * (2 * Hkv * D + dI) * esz
+        return kv, idx, qgo + new_rows
+
+    kv0, idx0, small0 = step_bytes(case.ctx)
+    per_step = kv0 + idx0 + small0
+    L = args.layers or max(2, math.ceil(3 * 256e6 / per_step))
+    total = args.warmup + args.steps
+    per_layer_steps = math.ceil(total / L) + 1
+    t0 = time.time()
+    dc = runner.DeviceCase(case, device=dev, n_layers=L, extra_steps=per_layer_steps)
+    log(f"[bench] {L} layer copies on the GPU in {time.time() - t0:.1f}s "
+        f"({per_step / 1e6:.1f} MB algorithmic per step)")
+
+    # Per-step inputs, drawn on the GPU with the workload's distributions, resident in HBM.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+    bf = torch.bfloat16
+
+    def nrm(shape, scale):
+        return (torch.randn(shape, generator=gen, device=dev) * scale).to(bf)
+
+    steps_in = []
+    for s in range(total):
+        steps_in.append({
+            "q": nrm((B, Hq, D), D ** -0.5), "k_new": nrm((B, Hkv, D), D ** -0.5),
+            "v_new": nrm((B, Hkv, D), D ** -0.5), "qI": nrm((B, HI, dI), dI ** -0.5),
+            "kI_new": nrm((B, dI), dI ** -0.5),
+            "w": torch.rand((B, HI), generator=gen, device=dev),
+            "gate": nrm((B, Hq, D), 1.0)})
+    batches = [dc.batch_for([c + j for c in case.ctx], [1] * B) for j in range(per_layer_steps)]
+    ws_bytes = max(qsa.qsa_workspace_size(dc.params, bt) for bt in batches)
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    outs = [torch.empty((B, Hq, D), dtype=bf, device=dev) for _ in range(total)]
+    sels = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(total)]
+    nbls = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(total)]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def fwd(s):
+        l, j = s % L, s // L
+        st, x = dc.layers[l], steps_in[s]
+        qsa.qsa_forward(dc.params, batches[j], x["q"], x["k_new"], x["v_new"], x["qI"],
+                        x["kI_new"], x["w"], x["gate"], st["k"], st["v"], st["kI"],
+                        st["pooled"], outs[s], sels[s], nbls[s], ws, sh)
+
+    for s in range(args.warmup):
+        fwd(s)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(args.warmup, total):
+        fwd(s)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tok_s = B / (ms_step * 1e-3)
+    hbm_gbps = per_step / (ms_step * 1e-3) / 1e9
+
+    # Dominant kernel: the attention of each timed step, launched alone on the
+    # same stream in the same layer rotation, bracketed by events.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for i, s in enumerate(range(args.warmup, total)):
+        l, j = s % L, s // L
+        st, x = dc.layers[l], steps_in[s]
+        ev[i][0].record(stream)
+        qsa.qsa_attend(dc.params, batches[j], x["q"], st["k"], st["v"], sels[s], nbls[s],
+                       x["gate"], outs[s], ws, sh)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    attn_bytes = kv0 + B * Hq * D * esz * 3
+    attn_gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; contexts U[8192,131072]; N(0,1)/sqrt(d) q/k/v)",
+        "config": {"workload": name, "batch": B, "ctx_min": min(case.ctx),
+                   "ctx_max": max(case.ctx), "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "block_size": r, "budget": sp.budget,
+                   "idx_heads": HI, "idx_dim": dI, "paged": bool(sp.page_size),
+                   "layer_copies": L},
+        "hbm_GBps_step": round(hbm_gbps, 1),
+        "hbm_frac_step": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "step_bytes": {"selected_kv": kv0, "pooled_keys": idx0, "q_gate_out_new_rows": small0},
+        "roofline": {"bound": "hbm", "kernel": "attention (qsa_attend)",
+                     "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+                     "avg_launch_us": round(attn_ms * 1e3, 2), "bytes_per_launch": attn_bytes,
+                     "traffic": None},
+    }
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, sp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(case, sp, seconds):
+    """The CPU oracle on the same step (each sequence's new token), threads
+    across sequences; repeated until about `seconds` of wall time."""
+    import concurrent.futures as cf
+    import oracle
+    from block_sparse_attention_keys_amd import workloads
+
+    orc = oracle.load()
+    cores = len(os.sched_getaffinity(0))
+    dims = dict(n_q_heads=sp.n_q_heads, n_kv_heads=sp.n_kv_heads, head_dim=sp.head_dim,
+                n_idx_heads=sp.n_idx_heads, idx_dim=sp.idx_dim, block_size=sp.block_size,
+                budget=sp.budget, attn_scale=0.0, idx_scale=0.0)
+    B = sp.n_seqs
+    f32 = [(workloads.as_f32(case.k[b]), workloads.as_f32(case.v[b]),
+            workloads.as_f32(case.kI[b])) for b in range(B)]
+
+    def one(b):
+        K, V, kI = f32[b]
+        p = case.ctx[b]
+        orc.sequence(dims, K, V, kI, np.array([p]), case.q[b][:1], case.qI[b][:1],
+                     case.w[b][:1], case.gate[b][:1])
+
+    threads = min(cores, B)
+    reps = 0
+    t0 = time.time()
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        while True:
+            list(ex.map(one, range(B)))
+            reps += 1
+            if time.time() - t0 >= seconds:
+                break
+    dt = time.time() - t0
+    return {"value": round(reps * B / dt, 2), "unit": "tok/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{reps} x one decode step of all {B} sequences (the same inputs), "
+                      f"threads over sequences, {dt:.1f}s wall",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,326 @@
+// C ABI of the QSA hot path: argument validation, workspace layout and launch
+// sequencing.  No arithmetic of the method happens here; every step runs in
+// the kernels of qsa_kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "qsa.h"
+#include "qsa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+qsa_status fail(qsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int ilog2(int64_t x) {
+  int l = 0;
+  while ((int64_t(1) << l) < x) ++l;
+  return l;
+}
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxK = 2048;
+
+struct Plan {
+  qsa::Geo geo;
+  qsa::AttnPlan attn;
+  int elem;
+  size_t off_scores, off_sel, off_nblk, off_part, total;
+};
+
+// Validates params/batch and derives every launch size from host values only.
+qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
+  if (P == nullptr || Bt == nullptr) return fail(QSA_ERR_INVALID, "params or batch is NULL");
+  const qsa_params& p = *P;
+  const qsa_batch& b = *Bt;
+  if (p.dtype != QSA_F32 && p.dtype != QSA_BF16)
+    return fail(QSA_ERR_INVALID, "dtype %d is neither QSA_F32 nor QSA_BF16", p.dtype);
+  if (p.n_q_heads <= 0 || p.n_kv_heads <= 0 || p.n_q_heads % p.n_kv_heads != 0)
+    return fail(QSA_ERR_INVALID, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                p.n_q_heads, p.n_kv_heads);
+  const int G = p.n_q_heads / p.n_kv_heads;
+  if (p.head_dim != 64 && p.head_dim != 128)
+    return fail(QSA_ERR_UNSUPPORTED, "head_dim %d: supported 64, 128", p.head_dim);
+  if (!qsa::attend_supported(G, p.head_dim))
+    return fail(QSA_ERR_UNSUPPORTED, "n_q_heads/n_kv_heads = %d: supported 1, 2, 4, 8, 16", G);
+  if (p.ratio != p.block_size)
+    return fail(QSA_ERR_INVALID,
+                "ratio (%d) must equal block_size (%d): the compression ratio is the block size",
+                p.ratio, p.block_size);
+  const int r = p.block_size;
+  int k = 0;
+  if (r != 0) {
+    if (r < 0 || !is_pow2(r) || r < 4 || r > 256)
+      return fail(QSA_ERR_UNSUPPORTED, "block_size %d: must be a power of two in [4, 256]", r);
+    if (p.budget < r)
+      return fail(QSA_ERR_INVALID, "budget (%d) must be >= block_size (%d)", p.budget, r);
+    k = p.budget / r;
+    if (k > kMaxK) return fail(QSA_ERR_UNSUPPORTED, "budget/block_size = %d exceeds %d", k, kMaxK);
+    if (p.n_idx_heads < 1 || p.n_idx_heads > 16)
+      return fail(QSA_ERR_UNSUPPORTED, "n_idx_heads %d: must be in [1, 16]", p.n_idx_heads);
+    if (p.idx_dim != 32 && p.idx_dim != 64 && p.idx_dim != 128)
+      return fail(QSA_ERR_UNSUPPORTED, "idx_dim %d: supported 32, 64, 128", p.idx_dim);
+  }
+  if (!(p.attn_scale == p.attn_scale) || !(p.idx_scale == p.idx_scale) || isinf(p.attn_scale) ||
+      isinf(p.idx_scale))
+    return fail(QSA_ERR_INVALID, "attn_scale / idx_scale must be finite");
+  if (b.n_seqs < 1) return fail(QSA_ERR_INVALID, "n_seqs (%d) must be >= 1", b.n_seqs);
+  if (b.n_tokens < 0) return fail(QSA_ERR_INVALID, "n_tokens (%d) must be >= 0", b.n_tokens);
+  if (b.n_tokens > 0) {
+    if (b.max_q_len < 1 || b.max_q_len > b.n_tokens)
+      return fail(QSA_ERR_INVALID, "max_q_len (%d) must be in [1, n_tokens=%d]", b.max_q_len,
+                  b.n_tokens);
+    if (b.max_kv_len < 1 || b.max_kv_len < b.max_q_len)
+      return fail(QSA_ERR_INVALID, "max_kv_len (%d) must be >= max_q_len (%d)", b.max_kv_len,
+                  b.max_q_len);
+    if (b.cu_q == nullptr || b.past_len == nullptr)
+      return fail(QSA_ERR_INVALID, "cu_q and past_len must be device pointers");
+  }
+  if (b.kv_capacity < b.max_kv_len)
+    return fail(QSA_ERR_INVALID, "kv_capacity (%d) < max_kv_len (%d)", b.kv_capacity,
+                b.max_kv_len);
+  if (b.page_size != 0) {
+    if (!is_pow2(b.page_size))
+      return fail(QSA_ERR_INVALID, "page_size %d must be a power of two", b.page_size);
+    if (b.page_table == nullptr) return fail(QSA_ERR_INVALID, "paged layout needs page_table");
+    if (b.max_pages < 1 || (int64_t)b.max_pages * b.page_size != b.kv_capacity)
+      return fail(QSA_ERR_INVALID, "paged layout needs kv_capacity == max_pages * page_size");
+    if (b.n_pages < 1) return fail(QSA_ERR_INVALID, "n_pages (%d) must be >= 1", b.n_pages);
+  } else if (b.page_table != nullptr) {
+    return fail(QSA_ERR_INVALID, "page_table given but page_size is 0");
+  }
+
+  Plan& pl = *out;
+  qsa::Geo& g = pl.geo;
+  g.Hq = p.n_q_heads;
+  g.Hkv = p.n_kv_heads;
+  g.G = G;
+  g.D = p.head_dim;
+  g.HI = r ? p.n_idx_heads : 0;
+  g.dI = r ? p.idx_dim : 0;
+  g.r = r;
+  g.log2r = r ? ilog2(r) : 0;
+  g.k = k;
+  g.B = b.n_seqs;
+  g.T = b.n_tokens;
+  g.cap = b.kv_capacity;
+  g.page_size = b.page_size;
+  g.log2ps = b.page_size ? ilog2(b.page_size) : 0;
+  g.max_pages = b.max_pages;
+  g.n_pages = b.n_pages;
+  g.pooled_ld = r ? (int32_t)round_up((b.kv_capacity + r - 1) / r, 64) : 0;
+  g.nbcap = r ? b.max_kv_len / r : 0;
+  const double a_scale = p.attn_scale > 0.0f ? (double)p.attn_scale : 1.0 / sqrt((double)g.D);
+  g.attn_scale_log2 = (float)(a_scale * 1.4426950408889634);
+  g.idx_scale = r ? (p.idx_scale > 0.0f ? p.idx_scale : (float)(1.0 / sqrt((double)g.dI))) : 0.0f;
+  g.inv_r = r ? 1.0f / (float)r : 0.0f;
+  g.cu_q = b.cu_q;
+  g.past_len = b.past_len;
+  g.page_table = b.page_table;
+  pl.elem = p.dtype == QSA_BF16 ? qsa::kBF16 : qsa::kF32;
+
+  // Split-KV plan: aim for about 2048 waves in flight.
+  const int64_t max_list = r ? std::min<int64_t>(b.max_kv_len, (int64_t)k * r + r - 1)
+                             : (int64_t)b.max_kv_len;
+  const int64_t tiles = std::max<int64_t>(1, (max_list + 63) / 64);
+  const int64_t units = std::max<int64_t>(1, (int64_t)b.n_tokens * g.Hkv);
+  int64_t splits = std::min<int64_t>(tiles, std::max<int64_t>(1, (2048 + units - 1) / units));
+  splits = std::min<int64_t>(splits, 65535);
+  const int64_t tps = (tiles + splits - 1) / splits;
+  splits = (tiles + tps - 1) / tps;
+  pl.attn.n_splits = (int32_t)splits;
+  pl.attn.split_tokens = (int32_t)(64 * tps);
+
+  const int64_t T = b.n_tokens;
+  size_t off = 0;
+  pl.off_scores = off;
+  off += round_up(T * std::max<int64_t>(g.nbcap, 1) * 4, kAlign);
+  pl.off_sel = off;
+  off += round_up(T * std::max(k, 1) * 4, kAlign);
+  pl.off_nblk = off;
+  off += round_up(T * 4, kAlign);
+  pl.off_part = off;
+  if (splits > 1) off += round_up(units * splits * G * (g.D + 2) * 4, kAlign);
+  pl.total = T > 0 ? off : 0;
+  if ((int64_t)g.T * g.Hkv > 0x7fffffff)
+    return fail(QSA_ERR_UNSUPPORTED, "n_tokens * n_kv_heads exceeds the grid limit");
+  return QSA_OK;
+}
+
+qsa_status check_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
+  if (pl.total == 0) return QSA_OK;
+  if (ws == nullptr || ws_bytes < pl.total)
+    return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                ws ? ws_bytes : (size_t)0, pl.total);
+  if (!aligned(ws, 16)) return fail(QSA_ERR_INVALID, "workspace must be 16-byte aligned");
+  return QSA_OK;
+}
+
+qsa_status need(const void* ptr, const char* name, size_t align) {
+  if (ptr == nullptr) return fail(QSA_ERR_INVALID, "%s is NULL", name);
+  if (!aligned(ptr, align)) return fail(QSA_ERR_INVALID, "%s is not %zu-byte aligned", name, align);
+  return QSA_OK;
+}
+
+#define QSA_TRY(x)                  \
+  do {                              \
+    qsa_status _s = (x);            \
+    if (_s != QSA_OK) return _s;    \
+  } while (0)
+
+qsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return QSA_OK;
+  return fail(QSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qsa_last_error(void) { return g_last_error.c_str(); }
+
+int64_t qsa_pooled_ld(const qsa_params* params, const qsa_batch* batch) {
+  Plan pl;
+  if (resolve(params, batch, &pl) != QSA_OK) return 0;
+  return pl.geo.pooled_ld;
+}
+
+size_t qsa_workspace_size(const qsa_params* params, const qsa_batch* batch) {
+  Plan pl;
+  if (resolve(params, batch, &pl) != QSA_OK) return 0;
+  return pl.total;
+}
+
+qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,
+                         const void* k_idx_new, void* k_idx_cache, float* pooled,
+                         void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  QSA_TRY(resolve(params, batch, &pl));
+  if (pl.geo.r == 0) return fail(QSA_ERR_INVALID, "dense layer (block_size 0) has no indexer");
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(need(k_idx_new, "k_idx_new", 16));
+  QSA_TRY(need(k_idx_cache, "k_idx_cache", 16));
+  QSA_TRY(need(pooled, "pooled", 16));
+  return hip_status(qsa::launch_append_pool(pl.geo, pl.elem, nullptr, nullptr, k_idx_new,
+                                            nullptr, nullptr, k_idx_cache, pooled,
+                                            static_cast<hipStream_t>(stream)),
+                    "qsa_pool_keys launch");
+}
+
+qsa_status qsa_score_select(const qsa_params* params, const qsa_batch* batch,
+                            const void* q_idx, const float* w, const float* pooled,
+                            int32_t* sel, int32_t* n_blocks, float* scores_opt, void* ws,
+                            size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  QSA_TRY(resolve(params, batch, &pl));
+  if (pl.geo.r == 0) return fail(QSA_ERR_INVALID, "dense layer (block_size 0) has no indexer");
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(need(q_idx, "q_idx", 16));
+  QSA_TRY(need(w, "w", 4));
+  QSA_TRY(need(pooled, "pooled", 16));
+  QSA_TRY(need(sel, "sel", 4));
+  QSA_TRY(need(n_blocks, "n_blocks", 4));
+  if (scores_opt != nullptr) QSA_TRY(need(scores_opt, "scores", 4));
+  QSA_TRY(check_ws(pl, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
+  QSA_TRY(hip_status(qsa::launch_score(pl.geo, pl.elem, q_idx, w, pooled, scores, st),
+                     "score launch"));
+  return hip_status(qsa::launch_select(pl.geo, scores, sel, n_blocks, st), "select launch");
+}
+
+qsa_status qsa_attend(const qsa_params* params, const qsa_batch* batch, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* sel,
+                      const int32_t* n_blocks, const void* gate, void* out, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  QSA_TRY(resolve(params, batch, &pl));
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(need(q, "q", 16));
+  QSA_TRY(need(k_cache, "k_cache", 16));
+  QSA_TRY(need(v_cache, "v_cache", 16));
+  QSA_TRY(need(gate, "gate", 16));
+  QSA_TRY(need(out, "out", 16));
+  if (pl.geo.r != 0) {
+    QSA_TRY(need(sel, "sel", 4));
+    QSA_TRY(need(n_blocks, "n_blocks", 4));
+  }
+  QSA_TRY(check_ws(pl, ws, ws_bytes));
+  float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
+  return hip_status(qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, sel,
+                                       n_blocks, gate, out, part,
+                                       static_cast<hipStream_t>(stream)),
+                    "attend launch");
+}
+
+qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const void* q,
+                       const void* k_new, const void* v_new, const void* q_idx,
+                       const void* k_idx_new, const float* w, const void* gate,
+                       void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                       void* out, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  QSA_TRY(resolve(params, batch, &pl));
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(need(q, "q", 16));
+  QSA_TRY(need(k_new, "k_new", 16));
+  QSA_TRY(need(v_new, "v_new", 16));
+  QSA_TRY(need(gate, "gate", 16));
+  QSA_TRY(need(k_cache, "k_cache", 16));
+  QSA_TRY(need(v_cache, "v_cache", 16));
+  QSA_TRY(need(out, "out", 16));
+  const bool qsa_layer = pl.geo.r != 0;
+  if (qsa_layer) {
+    QSA_TRY(need(q_idx, "q_idx", 16));
+    QSA_TRY(need(k_idx_new, "k_idx_new", 16));
+    QSA_TRY(need(w, "w", 4));
+    QSA_TRY(need(k_idx_cache, "k_idx_cache", 16));
+    QSA_TRY(need(pooled, "pooled", 16));
+    if (sel_opt) QSA_TRY(need(sel_opt, "sel", 4));
+    if (n_blocks_opt) QSA_TRY(need(n_blocks_opt, "n_blocks", 4));
+  }
+  QSA_TRY(check_ws(pl, ws, ws_bytes));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t* sel = sel_opt ? sel_opt : reinterpret_cast<int32_t*>(ws_at(ws, pl.off_sel));
+  int32_t* nblk = n_blocks_opt ? n_blocks_opt : reinterpret_cast<int32_t*>(ws_at(ws, pl.off_nblk));
+  QSA_TRY(hip_status(qsa::launch_append_pool(pl.geo, pl.elem, k_new, v_new,
+                                             qsa_layer ? k_idx_new : nullptr, k_cache, v_cache,
+                                             qsa_layer ? k_idx_cache : nullptr,
+                                             qsa_layer ? pooled : nullptr, st),
+                     "append/pool launch"));
+  if (qsa_layer) {
+    float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
+    QSA_TRY(hip_status(qsa::launch_score(pl.geo, pl.elem, q_idx, w, pooled, scores, st),
+                       "score launch"));
+    QSA_TRY(hip_status(qsa::launch_select(pl.geo, scores, sel, nblk, st), "select launch"));
+  }
+  float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
+  return hip_status(qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, sel, nblk,
+                                       gate, out, part, st),
+                    "attend launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal interface between the C-ABI host layer (qsa_api.hip) and the
+// gfx950 kernels (qsa_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+// Per-call geometry, passed to every kernel by value.
+struct Geo {
+  int32_t Hq, Hkv, G, D;       // query heads, KV heads, heads per KV head, head dim
+  int32_t HI, dI;              // indexer heads and dim
+  int32_t r, log2r, k;         // block size (0 = dense), log2, blocks kept
+  int32_t B, T;                // sequences, new tokens
+  int32_t cap;                 // rows per sequence
+  int32_t page_size, log2ps;   // 0 = contiguous
+  int32_t max_pages, n_pages;
+  int32_t pooled_ld;           // leading dim of the pooled cache
+  int32_t nbcap;               // row stride of the score buffer (max_kv_len / r)
+  float attn_scale_log2;       // attn_scale * log2(e): softmax runs in base 2
+  float idx_scale;             // indexer softmax scale (fp32, applied as c * d)
+  float inv_r;                 // 1 / r, exact because r is a power of two
+  const int32_t* cu_q;
+  const int32_t* past_len;
+  const int32_t* page_table;
+};
+
+// Split-KV plan of the attention kernels.
+struct AttnPlan {
+  int32_t n_splits;      // splits per (token, KV head)
+  int32_t split_tokens;  // tokens of the selection list per split (multiple of 64)
+};
+
+enum ElemType { kF32 = 0, kBF16 = 1 };
+
+// Launchers; each returns hipGetLastError() after its launches.
+hipError_t launch_append_pool(const Geo& g, int elem, const void* k_new, const void* v_new,
+                              const void* kI_new, void* k_cache, void* v_cache, void* kI_cache,
+                              float* pooled, hipStream_t st);
+hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w,
+                        const float* pooled, float* scores, hipStream_t st);
+hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
+                         hipStream_t st);
+hipError_t launch_attend(const Geo& g, int elem, const AttnPlan& plan, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* sel,
+                         const int32_t* n_blocks, const void* gate, void* out, float* part,
+                         hipStream_t st);
+
+// True when a kernel instantiation exists for G heads per KV head and dim D.
+bool attend_supported(int G, int D);
+
+}  // namespace qsa

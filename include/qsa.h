@@ -1,0 +1,167 @@
+/*
+ * qsa.h -- C ABI of the Qwen Sparse Attention (QSA) hot path on AMD Instinct
+ * MI355X (gfx950).  Library: libqsa.so (HIP kernels, no host-side compute).
+ *
+ * What is computed (per query token t of sequence b at position p, n = p+1):
+ *   1. Indexer keys are mean-pooled over complete blocks of r tokens
+ *      ("mean-pooled key blocks": MTPLX "Native Backend Components for the
+ *      Qwen4-Generation Preview Family", section "Qwen Sparse Attention").
+ *   2. Each candidate block j < floor(n/r) is scored
+ *        s_j = sum_h w[t,h] * relu(idx_scale * <q_idx[t,h], pooled_j>)
+ *      (DeepSeek-style indexer logits with head scale 1 and softmax scale
+ *      d_I^-0.5: llama.cpp PR #27739 page, LocalAI QSA-block commit, opening
+ *      paragraph).
+ *   3. The top k = budget / r blocks are kept (ties: lowest block index), plus
+ *      the incomplete tail [r*floor(n/r), n), which is always kept (dev.to
+ *      Qwen4-Exp article, section "Qwen Sparse Attention").  When
+ *      floor(n/r) <= k every candidate is kept ("Porting Qwen4 to llama.cpp",
+ *      section "QSA Should First Be Implemented as Selection Semantics").
+ *   4. Every kept token is <= p (the causal intersection), and gated GQA
+ *      softmax attention runs over exactly those tokens: query head h reads KV
+ *      head h / (Hq/Hkv); out = softmax(attn_scale * q K^T) V * sigmoid(gate),
+ *      elementwise ("selected block IDs -> direct indexed K/V loads -> online
+ *      softmax -> output accumulation": same porting article, section "CUDA
+ *      Optimization Should Follow State Correctness").
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers except the two structs are DEVICE pointers owned by the
+ *    caller; the library never allocates, frees or keeps device memory, and
+ *    holds no per-sequence state.  Save, restore and clone of the indexer
+ *    state are the caller's copies of k_idx_cache and pooled.
+ *  - stream is a hipStream_t (NULL = default stream).  Calls only enqueue
+ *    work: no host synchronisation and no device-to-host reads.
+ *  - Every argument is validated on the host BEFORE anything is enqueued; on
+ *    error nothing is launched, a status < 0 is returned and qsa_last_error()
+ *    gives the reason.  Device-side metadata (cu_q, past_len, page_table,
+ *    sel, n_blocks) cannot be checked on the host; the kernels skip rows whose
+ *    metadata falls outside the stated capacities instead of faulting.
+ *  - n_tokens == 0 is a no-op returning QSA_OK.
+ *  - Layouts (row-major, contiguous, element type = params.dtype unless said):
+ *      q, gate, out         [T][Hq][D]
+ *      k_new, v_new         [T][Hkv][D]
+ *      q_idx                [T][H_I][d_I]
+ *      k_idx_new            [T][d_I]
+ *      w                    [T][H_I]                      fp32
+ *      k_cache, v_cache     contiguous: [B][Hkv][kv_capacity][D]
+ *                           paged:      [n_pages][Hkv][page_size][D]
+ *      k_idx_cache          contiguous: [B][kv_capacity][d_I]
+ *                           paged:      [n_pages][page_size][d_I]
+ *      pooled               [B][d_I][pooled_ld]   fp32, column-major per
+ *                           sequence (block j of dimension x at x*pooled_ld+j),
+ *                           pooled_ld = qsa_pooled_ld(params, batch)
+ *      sel                  [T][k] int32, ascending block ids, -1 padded
+ *      n_blocks             [T] int32 = min(k, floor(n/r))
+ *      scores               [T][max_kv_len / r] fp32, -inf past floor(n/r)
+ *  - Token t belongs to sequence b with cu_q[b] <= t < cu_q[b+1]; its
+ *    position is past_len[b] + (t - cu_q[b]).
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_INVALID = -1,     /* bad argument or inconsistent sizes */
+  QSA_ERR_UNSUPPORTED = -2, /* valid, but a shape this build has no kernel for */
+  QSA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than qsa_workspace_size */
+  QSA_ERR_HIP = -4          /* a HIP launch failed; qsa_last_error has its text */
+} qsa_status;
+
+typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
+
+/* Layer geometry (host values). */
+typedef struct {
+  int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads;  /* Hkv; Hq/Hkv in {1,2,4,8,16} */
+  int32_t head_dim;    /* D in {64, 128} */
+  int32_t n_idx_heads; /* H_I in [1, 16] */
+  int32_t idx_dim;     /* d_I in {32, 64, 128} */
+  int32_t block_size;  /* r, a power of two in [4, 256]; 0 = dense layer (ratio 0
+                          marks a non-QSA layer: llama.cpp PR page, MTP commit) */
+  int32_t ratio;       /* the pages' compression ratio; must equal block_size */
+  int32_t budget;      /* tokens; k = budget / r in [1, 2048] (floor) */
+  float attn_scale;    /* <= 0 selects D^-0.5 */
+  float idx_scale;     /* <= 0 selects d_I^-0.5 */
+  int32_t dtype;       /* qsa_dtype of q, k, v, gate, out, q_idx, k_idx */
+} qsa_params;
+
+/* One call's batch (host sizes for launch geometry + device metadata). */
+typedef struct {
+  int32_t n_seqs;      /* B >= 1 */
+  int32_t n_tokens;    /* T = new tokens in this call, all sequences; >= 0 */
+  int32_t max_q_len;   /* >= max_b (cu_q[b+1]-cu_q[b]) */
+  int32_t max_kv_len;  /* >= max_b past_len[b] + new tokens of b */
+  int32_t kv_capacity; /* rows per sequence; paged: max_pages * page_size */
+  int32_t page_size;   /* 0 = contiguous caches; else a power of two */
+  int32_t max_pages;   /* columns of page_table (paged) */
+  int32_t n_pages;     /* physical pages in the cache pool (paged) */
+  const int32_t* cu_q;       /* [B+1] device, cu_q[0] = 0, cu_q[B] = T */
+  const int32_t* past_len;   /* [B] device, rows cached before this call */
+  const int32_t* page_table; /* [B][max_pages] device physical page ids, or NULL */
+} qsa_batch;
+
+/* Text of the last failure on the calling thread ("" if none). */
+const char* qsa_last_error(void);
+
+/* Leading dimension of the pooled cache: ceil(kv_capacity / r) rounded up to a
+ * multiple of 64.  Returns 0 for a dense layer or invalid arguments. */
+int64_t qsa_pooled_ld(const qsa_params* params, const qsa_batch* batch);
+
+/* Bytes of scratch workspace any entry point may need for this call (same
+ * value for every entry point; 0 when n_tokens == 0).  The workspace holds
+ * block scores, split-attention partials and, when the caller does not ask
+ * for them, the selections.  Its contents need no initialisation. */
+size_t qsa_workspace_size(const qsa_params* params, const qsa_batch* batch);
+
+/* Indexer-key append and incremental block pooling.
+ * Writes k_idx_new[t] to k_idx_cache row past_len[b] + (t - cu_q[b]) (row
+ * past_len, not row 0: LocalAI QSA-block commit, section "The battery"), then
+ * pools every block completed by this call:
+ *   pooled_j[x] = (sum over s = jr .. jr+r-1, ascending, of k_idx[s][x]) / r
+ * in fp32.  Only new blocks are touched, O(new tokens) -- not the whole-cache
+ * recompute of the upstream reference ("The trap the layer loop walks into").
+ * Dense layer (block_size 0): QSA_ERR_INVALID. */
+qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,
+                         const void* k_idx_new, void* k_idx_cache, float* pooled,
+                         void* stream);
+
+/* Block scoring and top-k selection (steps 2-3 above).
+ * Reads q_idx [T][H_I][d_I], w [T][H_I] and the pooled cache; writes sel and
+ * n_blocks; scores_opt (may be NULL) receives the pre-top-k scores, the value
+ * gate of the LocalAI QSA-block commit.  ws: qsa_workspace_size bytes. */
+qsa_status qsa_score_select(const qsa_params* params, const qsa_batch* batch,
+                            const void* q_idx, const float* w, const float* pooled,
+                            int32_t* sel, int32_t* n_blocks, float* scores_opt, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Gated GQA attention over the selected blocks plus the tail (step 4).
+ * The caches must already hold every token up to each query's position.
+ * sel / n_blocks as written by qsa_score_select (ignored for a dense layer,
+ * which attends all of [0, n)).  out [T][Hq][D]. */
+qsa_status qsa_attend(const qsa_params* params, const qsa_batch* batch, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* sel,
+                      const int32_t* n_blocks, const void* gate, void* out, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* The whole QSA layer step for one batch of new tokens: append k_new, v_new,
+ * k_idx_new to the caches at each sequence's past_len, pool the completed
+ * blocks, score, select, and attend.  sel_opt / n_blocks_opt (may be NULL)
+ * receive the selections.  A dense layer skips the indexer. */
+qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const void* q,
+                       const void* k_new, const void* v_new, const void* q_idx,
+                       const void* k_idx_new, const float* w, const void* gate,
+                       void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                       void* out, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
+                       size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -1,0 +1,109 @@
+"""Runs a workload through the C ABI on the GPU and compares it with the
+CPU oracle on the same seeded inputs (helpers for the GPU parity tests)."""
+from __future__ import annotations
+
+import sys
+from typing import Dict, List, Optional
+
+import numpy as np
+import torch
+
+import oracle
+import parity
+from block_sparse_attention_keys_amd import qsa, runner, workloads
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dims_of(dc: runner.DeviceCase) -> dict:
+    p = dc.params
+    return dict(n_q_heads=p.n_q_heads, n_kv_heads=p.n_kv_heads, head_dim=p.head_dim,
+                n_idx_heads=p.n_idx_heads, idx_dim=p.idx_dim, block_size=p.block_size,
+                budget=p.budget, attn_scale=p.attn_scale, idx_scale=p.idx_scale)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+class SeqF32:
+    """fp32 host views of a sequence's K, V, k_I (converted once)."""
+
+    def __init__(self, case: workloads.Case):
+        self.case = case
+        self.cache: Dict[int, tuple] = {}
+
+    def get(self, b):
+        if b not in self.cache:
+            c = self.case
+            self.cache[b] = (workloads.as_f32(c.k[b]), workloads.as_f32(c.v[b]),
+                             workloads.as_f32(c.kI[b]))
+        return self.cache[b]
+
+
+def run_calls(dc: runner.DeviceCase, calls: Optional[List[int]] = None, keep=None):
+    """Run calls in order; return per kept call (out, sel, n_blocks, spans)."""
+    n = len(dc.case.calls)
+    calls = list(range(n)) if calls is None else calls
+    res = {}
+    for i in calls:
+        inp = dc.call_inputs(i)
+        outs = dc.alloc_outputs(inp)
+        say(f"  gpu call {i}/{n}: T={inp['T']}")
+        dc.forward(inp, outs)
+        torch.cuda.synchronize()
+        if keep is None or i in keep:
+            res[i] = (to_np(outs["out"]), outs["sel"].cpu().numpy(),
+                      outs["n_blocks"].cpu().numpy(), inp["spans"])
+    return res
+
+
+def check_call(dc, seqf: SeqF32, result, sample: Optional[int] = None, rng_seed: int = 0,
+               orc=None) -> dict:
+    """Compare one call's GPU results with the oracle, all queries or a sample
+    of them per sequence.  Raises AssertionError on a miss."""
+    orc = orc or oracle.load()
+    out, sel, nblk, spans = result
+    case = dc.case
+    dims = dims_of(dc)
+    dtype = case.spec.dtype
+    rng = np.random.default_rng(rng_seed)
+    t0 = 0
+    worst = {"max_abs": 0.0, "mean_abs": 0.0, "max_rel": 0.0, "rows": 0, "exempt": 0}
+    for b, (s, e) in enumerate(spans):
+        n_q = e - s
+        idx = np.arange(n_q)
+        if sample is not None and n_q > sample:
+            idx = np.sort(rng.choice(n_q, size=sample, replace=False))
+        K, V, kI = seqf.get(b)
+        qbase = int(case.q_pos[b][0])
+        qi = (s - qbase) + idx
+        ref = orc.sequence(dims, K, V, kI, s + idx, case.q[b][qi], case.qI[b][qi],
+                           case.w[b][qi], case.gate[b][qi], want_scores=dims["block_size"] > 0)
+        got = out[t0 + idx]
+        ok, st = parity.outputs_ok(got, ref["out"], dtype)
+        assert ok, f"seq {b} outputs {st}"
+        if dims["block_size"] > 0:
+            r = dims["block_size"]
+            nb = (s + idx + 1) // r
+            k = ref["sel"].shape[1]
+            oks, ndiff, nex = parity.selections_ok(sel[t0 + idx][:, :k], nblk[t0 + idx],
+                                                   ref["sel"], ref["n_blocks"],
+                                                   ref.get("scores"), nb)
+            assert oks, f"seq {b}: selections differ in {ndiff} rows"
+            worst["exempt"] += nex
+        for kk in ("max_abs", "mean_abs", "max_rel"):
+            worst[kk] = max(worst[kk], st[kk])
+        worst["rows"] += len(idx)
+        t0 += n_q
+    return worst
+
+
+def pooled_rows(dc: runner.DeviceCase, layer=0) -> np.ndarray:
+    """The GPU pooled cache as [B][nb][d_I] (its layout is [B][d_I][ld])."""
+    return dc.layers[layer]["pooled"].permute(0, 2, 1).cpu().numpy()
