@@ -123,7 +123,7 @@ def main():
             "gate": nrm((B, Hq, D), 1.0)})
     batches = [dc.batch_for([c + j for c in case.ctx], [1] * B) for j in range(per_layer_steps)]
     ws_bytes = max(qsa.qsa_workspace_size(dc.params, bt) for bt in batches)
-    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
     outs = [torch.empty((B, Hq, D), dtype=bf, device=dev) for _ in range(total)]
     sels = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(total)]
     nbls = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(total)]

@@ -109,6 +109,7 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
 
   Plan& pl = *out;
   qsa::Geo& g = pl.geo;
+  pl.elem = p.dtype == QSA_BF16 ? qsa::kBF16 : qsa::kF32;
   g.Hq = p.n_q_heads;
   g.Hkv = p.n_kv_heads;
   g.G = G;
@@ -134,19 +135,21 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   g.cu_q = b.cu_q;
   g.past_len = b.past_len;
   g.page_table = b.page_table;
-  pl.elem = p.dtype == QSA_BF16 ? qsa::kBF16 : qsa::kF32;
 
-  // Split-KV plan: aim for about 2048 waves in flight.
+  // Split-KV plan: about 2048 waves in flight (8 per CU); each wave walks
+  // tpw 64-token tiles; a split is one workgroup of `waves` waves.
   const int64_t max_list = r ? std::min<int64_t>(b.max_kv_len, (int64_t)k * r + r - 1)
                              : (int64_t)b.max_kv_len;
   const int64_t tiles = std::max<int64_t>(1, (max_list + 63) / 64);
   const int64_t units = std::max<int64_t>(1, (int64_t)b.n_tokens * g.Hkv);
-  int64_t splits = std::min<int64_t>(tiles, std::max<int64_t>(1, (2048 + units - 1) / units));
-  splits = std::min<int64_t>(splits, 65535);
-  const int64_t tps = (tiles + splits - 1) / splits;
-  splits = (tiles + tps - 1) / tps;
+  const int64_t waves = qsa::attend_waves(pl.elem, g.D);
+  const int64_t max_splits = std::max<int64_t>(1, (tiles + waves - 1) / waves);
+  int64_t splits = std::max<int64_t>(1, (2048 + units * waves - 1) / (units * waves));
+  splits = std::min<int64_t>(std::min<int64_t>(splits, max_splits), qsa::kPlanMaxSplits);
+  const int64_t tpw = (tiles + splits * waves - 1) / (splits * waves);
+  splits = (tiles + waves * tpw - 1) / (waves * tpw);
   pl.attn.n_splits = (int32_t)splits;
-  pl.attn.split_tokens = (int32_t)(64 * tps);
+  pl.attn.split_tokens = (int32_t)(64 * waves * tpw);
 
   const int64_t T = b.n_tokens;
   size_t off = 0;
@@ -161,6 +164,11 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   pl.total = T > 0 ? off : 0;
   if ((int64_t)g.T * g.Hkv > 0x7fffffff)
     return fail(QSA_ERR_UNSUPPORTED, "n_tokens * n_kv_heads exceeds the grid limit");
+  // K/V cache rows are addressed by 32-bit row index inside the kernels.
+  const int64_t kv_rows = b.page_size ? (int64_t)b.n_pages * g.Hkv * b.page_size
+                                      : (int64_t)b.n_seqs * g.Hkv * b.kv_capacity;
+  if (kv_rows > 0x7fffffff)
+    return fail(QSA_ERR_UNSUPPORTED, "the K/V cache holds more than 2^31 rows");
   return QSA_OK;
 }
 

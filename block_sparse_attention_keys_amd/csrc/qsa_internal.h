@@ -28,9 +28,13 @@ struct Geo {
 
 // Split-KV plan of the attention kernels.
 struct AttnPlan {
-  int32_t n_splits;      // splits per (token, KV head)
-  int32_t split_tokens;  // tokens of the selection list per split (multiple of 64)
+  int32_t n_splits;      // splits per (token, KV head), <= kPlanMaxSplits
+  int32_t split_tokens;  // tokens of the selection list per split (multiple of 64 * waves)
 };
+constexpr int kPlanMaxSplits = 128;
+
+// Waves per workgroup of the attention kernel chosen for this dtype / head dim.
+inline int attend_waves(int elem, int D) { return (elem == 1 && D == 128) ? 4 : 1; }
 
 enum ElemType { kF32 = 0, kBF16 = 1 };
 

@@ -30,8 +30,7 @@ namespace qsa {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
+typedef __attribute__((address_space(4))) const uint32_t CU32;  // constant (scalar) memory
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(uint16_t x) {
@@ -56,25 +55,46 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Wave-wide reductions: four DPP steps inside each row of 16 lanes (xor 1,
+// xor 2, half-row mirror, row mirror), then two cross-row exchanges.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp<0x140>(v));  // row_mirror
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
   return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  v += dpp<0x141>(v);
+  v += dpp<0x140>(v);
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
   return v;
 }
 
-// Sequence of token t: the largest b with cu_q[b] <= t.
+// Sequence of token t: the largest b with cu_q[b] <= t (cu_q ascending,
+// cu_q[0] = 0).  The wave reads 64 offsets at a time and counts them with a
+// ballot, so a batch of up to 64 sequences costs one memory round trip
+// instead of a chain of log2(B) dependent loads.  Wave-uniform result.
 __device__ __forceinline__ int seq_of(const int32_t* cu_q, int B, int t) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int b0 = 1; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const bool le = (b < B) && (cu_q[b] <= t);
+    const int c = __popcll(__ballot(le));
+    count += c;
+    if (c < 64) break;
   }
-  return lo;
+  return count;
 }
 
 struct QueryPos {
@@ -147,83 +167,99 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
   }
   // The token that ends block j pools it.  Rows appended by this same call are
   // read from kI_new (another workgroup may not have stored them yet); older
-  // rows come from the cache.
+  // rows come from the cache.  The rows are staged in LDS by all threads in
+  // parallel (64 at a time); then one thread per column adds them in token
+  // order, so the sum is the sequential fp32 sum.
   if (pooled == nullptr || g.r == 0 || ((qp.p + 1) & (g.r - 1)) != 0) return;
+  __shared__ float stage[64 * 128];
   const int j = qp.p >> g.log2r;
   const int past = g.past_len[qp.b], t0 = g.cu_q[qp.b];
-  for (int x = tid; x < g.dI; x += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = j << g.log2r; s <= qp.p; ++s) {
+  const int dI = g.dI;
+  float acc = 0.0f;
+  for (int s0 = j << g.log2r; s0 <= qp.p; s0 += 64) {
+    const int nrow = min(64, qp.p + 1 - s0);
+    for (int e = tid; e < nrow * dI; e += blockDim.x) {
+      const int rr = e / dI, x = e - rr * dI;
+      const int s = s0 + rr;
       float v = 0.0f;
       if (s >= past) {
-        v = to_f32(kI_new[(int64_t)(t0 + s - past) * g.dI + x]);
+        v = to_f32(kI_new[(int64_t)(t0 + s - past) * dI + x]);
       } else {
         const int64_t row = idx_row(g, qp.b, s);
         if (row >= 0) v = to_f32(kI_cache[row + x]);
       }
-      acc = acc + v;
+      stage[e] = v;
     }
-    pooled[((int64_t)qp.b * g.dI + x) * g.pooled_ld + j] = acc * g.inv_r;
+    __syncthreads();
+    if (tid < dI) {
+      for (int rr = 0; rr < nrow; ++rr) acc = acc + stage[rr * dI + tid];
+    }
+    __syncthreads();
   }
+  if (tid < dI) pooled[((int64_t)qp.b * dI + tid) * g.pooled_ld + j] = acc * g.inv_r;
 }
 
 // ---------------------------------------------------------------------------
-// score: grid (T, ceil(nbcap/256)), one wave; lane owns blocks j0..j0+3.
-template <typename E, int HIM>
+// score: grid (T, ceil(nbcap/64)), one wave, one lane per candidate block.
+// The pooled cache is column-major per sequence, so for each dimension x the
+// wave reads 64 consecutive blocks (256 contiguous bytes).
+template <typename E, int HIM, int DI>
 __global__ __launch_bounds__(64) void score_kernel(Geo g, const E* __restrict__ qI,
                                                    const float* __restrict__ w,
                                                    const float* __restrict__ pooled,
                                                    float* __restrict__ scores) {
-  __shared__ float qT[128 * HIM];  // [x][h]
+  __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
   __shared__ float wsh[HIM];
   const int t = blockIdx.x, lane = threadIdx.x;
   const QueryPos qp = query_pos(g, t);
   const int nb = qp.ok ? ((qp.p + 1) >> g.log2r) : 0;
-  const int j0 = blockIdx.y * 256 + lane * 4;
+  const int j = blockIdx.y * 64 + lane;
   float* srow = scores + (int64_t)t * g.nbcap;
-  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if ((int)blockIdx.y * 256 < nb) {
-    const int HI = g.HI, dI = g.dI;
-    for (int e = lane; e < dI * HIM; e += 64) {
+  float s = 0.0f;
+  if ((int)blockIdx.y * 64 < nb) {
+    const int HI = g.HI;
+    for (int e = lane; e < DI * HIM; e += 64) {
       const int x = e / HIM, h = e - x * HIM;
-      qT[e] = h < HI ? to_f32(qI[((int64_t)t * HI + h) * dI + x]) : 0.0f;
+      qT[e] = h < HI ? to_f32(qI[((int64_t)t * HI + h) * DI + x]) : 0.0f;
     }
     if (lane < HIM) wsh[lane] = lane < HI ? w[(int64_t)t * HI + lane] : 0.0f;
     __syncthreads();
-    if (j0 < nb) {
-      float acc[HIM][4];
+    if (j < nb) {
+      const float* pb = pooled + (int64_t)qp.b * DI * g.pooled_ld + j;
+      float acc[HIM];
 #pragma unroll
-      for (int h = 0; h < HIM; ++h) acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.0f;
-      const float* pb = pooled + (int64_t)qp.b * dI * g.pooled_ld + j0;
-      for (int x = 0; x < dI; ++x) {
-        const float4 pk = *reinterpret_cast<const float4*>(pb + (int64_t)x * g.pooled_ld);
+      for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
+      // 16 dimensions per trip: their loads are all in flight, then each
+      // head's chain advances x in ascending order.
+#pragma unroll 1
+      for (int x0 = 0; x0 < DI; x0 += 16) {
+        float pk[16];
 #pragma unroll
-        for (int h = 0; h < HIM; ++h) {
-          const float qv = qT[x * HIM + h];
-          acc[h][0] = fmaf(qv, pk.x, acc[h][0]);
-          acc[h][1] = fmaf(qv, pk.y, acc[h][1]);
-          acc[h][2] = fmaf(qv, pk.z, acc[h][2]);
-          acc[h][3] = fmaf(qv, pk.w, acc[h][3]);
+        for (int xx = 0; xx < 16; ++xx) pk[xx] = pb[(int64_t)(x0 + xx) * g.pooled_ld];
+#pragma unroll
+        for (int xx = 0; xx < 16; ++xx) {
+          const float4* qrow = reinterpret_cast<const float4*>(qT + (x0 + xx) * HIM);
+#pragma unroll
+          for (int h4 = 0; h4 < HIM / 4; ++h4) {
+            const float4 qv = qrow[h4];
+            acc[4 * h4 + 0] = fmaf(qv.x, pk[xx], acc[4 * h4 + 0]);
+            acc[4 * h4 + 1] = fmaf(qv.y, pk[xx], acc[4 * h4 + 1]);
+            acc[4 * h4 + 2] = fmaf(qv.z, pk[xx], acc[4 * h4 + 2]);
+            acc[4 * h4 + 3] = fmaf(qv.w, pk[xx], acc[4 * h4 + 3]);
+          }
         }
       }
 #pragma unroll
       for (int h = 0; h < HIM; ++h) {
         if (h < HI) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float a = g.idx_scale * acc[h][i];
-            a = (a > 0.0f) ? a : 0.0f;
-            s[i] = fmaf(wsh[h], a, s[i]);
-          }
+          float a = g.idx_scale * acc[h];
+          a = (a > 0.0f) ? a : 0.0f;
+          s = fmaf(wsh[h], a, s);
         }
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int j = j0 + i;
-    if (j < g.nbcap) srow[j] = (j < nb) ? s[i] : -INFINITY;
-  }
+  if (j < g.nbcap) srow[j] = (j < nb) ? s : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -250,14 +286,145 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
   return off + x - v;
 }
 
-// select: one 256-thread workgroup per query.
-__global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restrict__ scores,
-                                                     int32_t* __restrict__ sel,
-                                                     int32_t* __restrict__ n_blocks) {
+// Exclusive prefix sum over one wave.
+__device__ __forceinline__ int wave_excl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x - v;
+}
+
+// select: one 256-thread workgroup per query.  Thread tid owns the contiguous
+// candidates [tid*per, tid*per + per); with per <= 8 (nb <= 2048) their keys
+// stay in registers across the passes.
+//   4 passes of an 8-bit radix select find the k-th largest key K and how
+//   many keys equal to K are kept (the lowest-index ones: ties go to the
+//   lowest block index); a final pass writes the kept ids in ascending order.
+template <bool CACHED>
+__device__ __forceinline__ void select_impl(const Geo& g, const float* __restrict__ srow, int nb,
+                                            int32_t* __restrict__ out) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t s_prefix;
   __shared__ int s_want;
   __shared__ int sh[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, k = g.k;
+  const int per = (nb + 255) >> 8;
+  const int jb = tid * per;
+  const int jn = max(0, min(per, nb - jb));  // candidates this thread owns
+  uint32_t kr[8];
+  if (CACHED) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kr[e] = e < jn ? score_key(srow[jb + e]) : 0u;
+  }
+  uint32_t prefix = 0, mask = 0;
+  int want = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    if (CACHED) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < jn && (kr[e] & mask) == prefix) atomicAdd(&hist[(kr[e] >> shift) & 255u], 1u);
+    } else {
+      for (int e = 0; e < jn; ++e) {
+        const uint32_t key = score_key(srow[jb + e]);
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+    }
+    __syncthreads();
+    if (wid == 0) {
+      // lane owns digits 255-4*lane .. 252-4*lane (descending)
+      int c[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = (int)hist[255 - 4 * lane - i];
+        tot += c[i];
+      }
+      int above = wave_excl_scan(tot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < want && above + c[i] >= want) {
+          s_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
+          s_want = want - above;
+        }
+        above += c[i];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    want = s_want;
+    mask |= 255u << shift;
+  }
+  // Keep keys > prefix, and the first `want` keys == prefix in index order.
+  // Pass 1 counts equal keys (for their global rank) and kept keys; pass 2
+  // writes the kept ids at their ascending positions.
+  int n_eq = 0;
+  if (CACHED) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n_eq += (e < jn && kr[e] == prefix) ? 1 : 0;
+  } else {
+    for (int e = 0; e < jn; ++e) n_eq += (score_key(srow[jb + e]) == prefix) ? 1 : 0;
+  }
+  int tot;
+  const int eq_before = block_excl_scan(n_eq, &tot, sh);
+  int n_take = 0;
+  {
+    int eqr = eq_before;
+    if (CACHED) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e < jn) {
+          const bool eq = kr[e] == prefix;
+          n_take += (kr[e] > prefix || (eq && eqr < want)) ? 1 : 0;
+          eqr += eq ? 1 : 0;
+        }
+      }
+    } else {
+      for (int e = 0; e < jn; ++e) {
+        const uint32_t key = score_key(srow[jb + e]);
+        const bool eq = key == prefix;
+        n_take += (key > prefix || (eq && eqr < want)) ? 1 : 0;
+        eqr += eq ? 1 : 0;
+      }
+    }
+  }
+  int pos = block_excl_scan(n_take, &tot, sh);
+  {
+    int eqr = eq_before;
+    if (CACHED) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e < jn) {
+          const bool eq = kr[e] == prefix;
+          if (kr[e] > prefix || (eq && eqr < want)) {
+            if (pos < k) out[pos] = jb + e;
+            ++pos;
+          }
+          eqr += eq ? 1 : 0;
+        }
+      }
+    } else {
+      for (int e = 0; e < jn; ++e) {
+        const uint32_t key = score_key(srow[jb + e]);
+        const bool eq = key == prefix;
+        if (key > prefix || (eq && eqr < want)) {
+          if (pos < k) out[pos] = jb + e;
+          ++pos;
+        }
+        eqr += eq ? 1 : 0;
+      }
+    }
+  }
+  (void)lane;
+}
+
+__global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restrict__ scores,
+                                                     int32_t* __restrict__ sel,
+                                                     int32_t* __restrict__ n_blocks) {
   const int t = blockIdx.x, tid = threadIdx.x, k = g.k;
   const QueryPos qp = query_pos(g, t);
   // (min with the score row length only matters for inconsistent metadata)
@@ -269,45 +436,8 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restr
     return;
   }
   const float* srow = scores + (int64_t)t * g.nbcap;
-  uint32_t prefix = 0, mask = 0;
-  int want = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int j = tid; j < nb; j += 256) {
-      const uint32_t key = score_key(srow[j]);
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    const int d = 255 - tid;  // thread order = descending digit
-    const int c = static_cast<int>(hist[d]);
-    int tot;
-    const int above = block_excl_scan(c, &tot, sh);  // matching keys with digit > d
-    if (above < want && above + c >= want) {
-      s_prefix = prefix | (static_cast<uint32_t>(d) << shift);
-      s_want = want - above;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    want = s_want;
-    mask |= 255u << shift;
-  }
-  // prefix is the k-th largest key; keep every larger key and the `want`
-  // lowest-index keys equal to it, written in ascending block order.
-  int base = 0, eq_base = 0;
-  for (int c0 = 0; c0 < nb; c0 += 256) {
-    const int j = c0 + tid;
-    const uint32_t key = j < nb ? score_key(srow[j]) : 0u;
-    const int gt = (j < nb) && key > prefix;
-    const int eq = (j < nb) && key == prefix;
-    int eq_tot, take_tot;
-    const int eq_rank = eq_base + block_excl_scan(eq, &eq_tot, sh);
-    const int take = gt || (eq && eq_rank < want);
-    const int pos = base + block_excl_scan(take, &take_tot, sh);
-    if (take && pos < k) out[pos] = j;
-    base += take_tot;
-    eq_base += eq_tot;
-  }
+  if (nb <= 2048) select_impl<true>(g, srow, nb, out);
+  else select_impl<false>(g, srow, nb, out);
   if (tid == 0) n_blocks[t] = k;
 }
 
@@ -353,6 +483,80 @@ __device__ __forceinline__ int list_token(const Geo& g, const ListInfo& L,
   }
   return L.tail0 + (i - L.nsel_tok);
 }
+
+// Wave-local ordering of LDS traffic (the waves of a workgroup run different
+// numbers of tiles, so the tile loop cannot use workgroup barriers).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Split merge: one workgroup per (token, KV head) unit, launched after the
+// attention kernel (the kernel boundary makes every split's partial visible).
+// Partials: [split][G][D] o, then [G] m, then [G] l (base-2 log-sum-exp
+// state).  The (m, l) of all splits are staged in LDS first, so the o loads of
+// all splits are independent and in flight together; then the sigmoid gate.
+template <typename E, int G, int D, int MAXS>
+__global__ __launch_bounds__(256) void attn_combine_kernel(Geo g, AttnPlan plan,
+                                                           const float* __restrict__ part,
+                                                           const E* __restrict__ gate,
+                                                           E* __restrict__ out) {
+  constexpr int NT = 256;
+  constexpr int SP = G * (D + 2);
+  __shared__ float wgt[MAXS * G];   // m, then the split weight
+  __shared__ float lsp[MAXS * G];   // l
+  __shared__ float Linv[G];
+  const int unit = blockIdx.x, tid = threadIdx.x;
+  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv, h0 = kvh * G;
+  const QueryPos qp = query_pos(g, t);
+  if (!qp.ok) return;
+  const int n_splits = plan.n_splits;
+  const float* P0 = part + (int64_t)unit * n_splits * SP;
+  for (int e = tid; e < n_splits * G; e += NT) {
+    const int sp = e / G, h = e - sp * G;
+    wgt[e] = P0[(int64_t)sp * SP + G * D + h];
+    lsp[e] = P0[(int64_t)sp * SP + G * D + G + h];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, wgt[sp * G + tid]);
+    float L = 0.0f;
+    for (int sp = 0; sp < n_splits; ++sp) {
+      const float m = wgt[sp * G + tid];
+      const float w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
+      wgt[sp * G + tid] = w;
+      L = fmaf(lsp[sp * G + tid], w, L);
+    }
+    Linv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
+  }
+  __syncthreads();
+  constexpr int EPT = (G * D >= NT) ? G * D / NT : 1;  // elements per thread, inside one head
+  static_assert(D % EPT == 0, "combine layout");
+  const int e0 = tid * EPT, h = e0 / D, d0 = e0 - h * D;
+  if (e0 >= G * D) return;
+  float O[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) O[i] = 0.0f;
+#pragma unroll 4
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float w = wgt[sp * G + h];
+    const float* src = P0 + (int64_t)sp * SP + h * D + d0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) O[i] = fmaf(src[i], w, O[i]);
+  }
+  const float inv = Linv[h];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int64_t idx = ((int64_t)t * g.Hq + h0 + h) * D + d0 + i;
+    const float sg = 1.0f / (1.0f + expf(-to_f32(gate[idx])));
+    out[idx] = from_f32<E>(O[i] * inv * sg);
+  }
+}
+
+constexpr int kWaves = 4;       // waves per workgroup of the bf16 D=128 kernel
+constexpr int kMaxSplits = 128;  // splits per unit (bounded by the host plan)
 
 template <typename E, int G, int D>
 __global__ __launch_bounds__(64) void attn_split_kernel(
@@ -507,32 +711,245 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   }
 }
 
-template <typename E, int G, int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(Geo g, AttnPlan plan,
-                                                           const float* __restrict__ part,
-                                                           const E* __restrict__ gate,
-                                                           E* __restrict__ out) {
-  const int unit = blockIdx.x;
+// bf16, D = 128: the decode-bandwidth kernel.  A workgroup of 4 waves owns one
+// split of one (token, KV head) unit; its waves take the split's 64-token
+// tiles in turn.  Per tile, in one wave:
+//   1. each lane holds the cache row of one token (resolved one tile ahead,
+//      while the previous tile's loads are in flight);
+//   2. K and V of the tile are loaded up front in 16-byte chunks, 4 rows per
+//      instruction (fully coalesced): lane l holds chunk l%16 of the tokens
+//      l/16 + 4j, j = 0..15;
+//   3. K goes through padded LDS so that QK runs lane-per-token, as bf16 dot2
+//      against the query, which sits in scalar registers;
+//   4. online softmax in base 2, one max per head per tile;
+//   5. V stays in registers: each lane accumulates its 8 dims for its 16
+//      tokens, pairing tokens for bf16 dot2 with the probabilities rounded to
+//      bf16 (the denominator sums the same rounded values).
+// The 4 waves merge in LDS; a unit with several splits writes one partial per
+// split, merged by attn_combine_kernel.
+template <int G>
+__global__ __launch_bounds__(256) void attn_bf16_d128_kernel(
+    Geo g, AttnPlan plan, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
+    uint16_t* __restrict__ out, float* __restrict__ part) {
+  constexpr int D = 128;
+  constexpr int KS = 272;  // LDS row stride in bytes: 256 + 16 keeps ds_read_b128 conflict-free
+  constexpr int RR = 1024;  // rows resolved per round (4 tiles per wave)
+  __shared__ __attribute__((aligned(16))) unsigned char Ks_all[kWaves][64 * KS];
+  __shared__ int32_t rowidx[RR];                   // cache row (element offset / D), -1 = masked
+  __shared__ uint32_t PP_all[kWaves][4 * 8 * G];  // bf16 pairs of p: [token group][pair][head]
+  __shared__ float wm[kWaves][G], wl[kWaves][G];
+
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  unsigned char* Ks = Ks_all[wid];
+  uint32_t* PP = PP_all[wid];
   const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
   const QueryPos qp = query_pos(g, t);
-  if (!qp.ok) return;
-  const float* P0 = part + (int64_t)unit * plan.n_splits * (G * (D + 2));
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int h = e / D, d = e - h * D;
-    float M = -INFINITY;
-    for (int s = 0; s < plan.n_splits; ++s) M = fmaxf(M, P0[s * (G * (D + 2)) + G * D + h]);
-    float Lsum = 0.0f, O = 0.0f;
-    for (int s = 0; s < plan.n_splits; ++s) {
-      const float* P = P0 + s * (G * (D + 2));
-      const float ms = P[G * D + h];
-      if (ms == -INFINITY) continue;
-      const float wgt = exp2f(ms - M);
-      Lsum = fmaf(P[G * D + G + h], wgt, Lsum);
-      O = fmaf(P[h * D + d], wgt, O);
+  const ListInfo L = list_info(g, qp, nblk, t);
+  const int i0 = split * plan.split_tokens;
+  const int i1 = min(i0 + plan.split_tokens, L.n_list);
+  const int h0 = kvh * G;
+  const int grp = lane >> 4, cq = lane & 15;
+  const uint4* qv = reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0) * D);
+  const int32_t* srow = sel + (int64_t)t * g.k;
+
+  auto resolve = [&](int i) -> int32_t {
+    if (i >= i1) return -1;
+    const int s = list_token(g, L, srow, i);
+    const int64_t r = (s >= 0 && s <= qp.p) ? kv_row(g, qp.b, kvh, s) : -1;
+    return r >= 0 ? (int32_t)(r / D) : -1;
+  };
+
+  float m[G], ls[G], o[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    ls[h] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[h][d] = 0.0f;
+  }
+
+  // The split is walked in rounds of RR list positions: first the whole
+  // round's cache rows are resolved into LDS (selection entry, then page
+  // table: two dependent loads, paid once per round), then the waves take the
+  // round's 64-token tiles in turn.
+  for (int r0 = i0; r0 < i1; r0 += RR) {
+    __syncthreads();  // the previous round's rows are no longer read
+    for (int e = threadIdx.x; e < RR; e += 64 * kWaves) rowidx[e] = resolve(r0 + e);
+    __syncthreads();
+    const int r1 = min(r0 + RR, i1);
+  for (int it = r0 + 64 * wid; it < r1; it += 64 * kWaves) {
+    const int32_t* rows = rowidx + (it - r0);
+    const int32_t row = rows[lane];
+    // Full tiles (the common case) load unconditionally; a tile with an
+    // invalid row clamps its address to row 0 and zeroes what it loaded, so a
+    // masked token contributes exactly 0 even if row 0 holds NaN.
+    const bool full = __all(row >= 0);
+    uint4 vr[16];
+    {
+      uint4 kr[16];
+      int64_t ra[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int32_t rj = rows[grp + 4 * j];
+        ra[j] = rj >= 0 ? (int64_t)rj * D : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) kr[j] = *reinterpret_cast<const uint4*>(kc + ra[j] + cq * 8);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) vr[j] = *reinterpret_cast<const uint4*>(vc + ra[j] + cq * 8);
+      if (!full) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          if (rows[grp + 4 * j] < 0) {
+            kr[j] = make_uint4(0u, 0u, 0u, 0u);
+            vr[j] = make_uint4(0u, 0u, 0u, 0u);
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        *reinterpret_cast<uint4*>(Ks + (grp + 4 * j) * KS + cq * 16) = kr[j];
     }
-    const int64_t idx = ((int64_t)t * g.Hq + kvh * G + h) * D + d;
-    const float sg = 1.0f / (1.0f + expf(-to_f32(gate[idx])));
-    out[idx] = from_f32<E>(Lsum > 0.0f ? O / Lsum * sg : 0.0f);
+    wave_sync();
+
+    float z[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) z[h] = 0.0f;
+    const unsigned char* krow = Ks + lane * KS;
+    // Kept rolled (2 chunks per trip): each trip holds 2 x 4G query words in
+    // SGPRs; a full unroll would hoist all 64G words and spill.
+#pragma unroll 2
+    for (int c = 0; c < 16; ++c) {
+      const uint4 kk = *reinterpret_cast<const uint4*>(krow + c * 16);
+      // The query is wave-uniform: read it through the constant address
+      // space (scalar loads into SGPRs, the dot2's scalar operand).  The
+      // opaque pointer keeps each chunk's loads here instead of hoisted.
+      CU32* qc = (CU32*)(qv + c);
+      asm volatile("" : "+s"(qc));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        uint4 qq;
+        qq.x = qc[h * 64 + 0];
+        qq.y = qc[h * 64 + 1];
+        qq.z = qc[h * 64 + 2];
+        qq.w = qc[h * 64 + 3];
+        z[h] = dot2_bf16(kk.x, qq.x, z[h]);
+        z[h] = dot2_bf16(kk.y, qq.y, z[h]);
+        z[h] = dot2_bf16(kk.z, qq.z, z[h]);
+        z[h] = dot2_bf16(kk.w, qq.w, z[h]);
+      }
+    }
+
+    uint16_t* pp16 = reinterpret_cast<uint16_t*>(PP);
+    const int pslot = ((lane & 3) * 8 + (lane >> 3)) * G;  // this token's pair row
+    const int phalf = (lane >> 2) & 1;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float zz = (row >= 0) ? z[h] * g.attn_scale_log2 : -INFINITY;
+      const float mn = fmaxf(m[h], wave_max(zz));
+      const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2f(m[h] - mn);
+      const uint16_t pb = (zz == -INFINITY) ? (uint16_t)0 : bf16_rne(exp2f(zz - mn));
+      ls[h] = fmaf(ls[h], alpha, to_f32(pb));
+      m[h] = mn;
+#pragma unroll
+      for (int d = 0; d < 8; ++d) o[h][d] *= alpha;
+      pp16[(pslot + h) * 2 + phalf] = pb;
+    }
+    wave_sync();
+
+#pragma unroll
+    for (int mp = 0; mp < 8; ++mp) {
+      const uint4 va = vr[2 * mp], vb = vr[2 * mp + 1];
+      uint32_t vp[8];
+      vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
+      vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
+      vp[2] = __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u);
+      vp[3] = __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u);
+      vp[4] = __builtin_amdgcn_perm(vb.z, va.z, 0x05040100u);
+      vp[5] = __builtin_amdgcn_perm(vb.z, va.z, 0x07060302u);
+      vp[6] = __builtin_amdgcn_perm(vb.w, va.w, 0x05040100u);
+      vp[7] = __builtin_amdgcn_perm(vb.w, va.w, 0x07060302u);
+      const uint32_t* pr = PP + (grp * 8 + mp) * G;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const uint32_t pw = pr[h];
+#pragma unroll
+        for (int d = 0; d < 8; ++d) o[h][d] = dot2_bf16(pw, vp[d], o[h][d]);
+      }
+    }
+    wave_sync();
+  }
+  }
+
+  // Wave totals: l over all lanes, o over the four token groups.
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float lt = wave_sum(ls[h]);
+    if (lane == 0) {
+      wm[wid][h] = m[h];
+      wl[wid][h] = lt;
+    }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      o[h][d] += __shfl_xor(o[h][d], 16, 64);
+      o[h][d] += __shfl_xor(o[h][d], 32, 64);
+    }
+  }
+  // This wave's o -> its LDS region as fp32 [G][D] (group grp writes heads h%4 == grp).
+  float* wo = reinterpret_cast<float*>(Ks);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if ((h & 3) != grp) continue;
+    float4* dst = reinterpret_cast<float4*>(wo + h * D + cq * 8);
+    dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+    dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+  }
+  __syncthreads();
+
+  // Merge the 4 waves: thread -> EPT consecutive elements of one head.
+  constexpr int EPT = (G * D >= 256) ? G * D / 256 : 1;
+  const int tid = threadIdx.x;
+  const bool has_elem = tid * EPT < G * D;
+  const int e0 = has_elem ? tid * EPT : 0, hh = e0 / D, d0 = e0 - hh * D;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w][hh]);
+  float Lw = 0.0f, Ow[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) Ow[i] = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const float mw = wm[w][hh];
+    const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+    Lw = fmaf(wl[w][hh], a, Lw);
+    const float* src = reinterpret_cast<const float*>(Ks_all[w]) + hh * D + d0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) Ow[i] = fmaf(src[i], a, Ow[i]);
+  }
+
+  if (plan.n_splits == 1) {
+    if (!qp.ok || !has_elem) return;
+    const float inv = Lw > 0.0f ? 1.0f / Lw : 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int64_t idx = ((int64_t)t * g.Hq + h0 + hh) * D + d0 + i;
+      const float sg = 1.0f / (1.0f + expf(-to_f32(gate[idx])));
+      out[idx] = from_f32<uint16_t>(Ow[i] * inv * sg);
+    }
+    return;
+  }
+  constexpr int SP = G * (D + 2);
+  float* P = part + ((int64_t)unit * plan.n_splits + split) * SP;
+  if (has_elem) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) P[hh * D + d0 + i] = Ow[i];
+  }
+  if (has_elem && d0 == 0) {
+    P[G * D + hh] = M;
+    P[G * D + G + hh] = Lw;
   }
 }
 
@@ -541,12 +958,19 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
                        const void* v_cache, const int32_t* sel, const int32_t* n_blocks,
                        const void* gate, void* out, float* part, hipStream_t st) {
   dim3 grid(g.T * g.Hkv, plan.n_splits);
-  attn_split_kernel<E, G, D><<<grid, 64, 0, st>>>(
-      g, plan, static_cast<const E*>(q), static_cast<const E*>(k_cache),
-      static_cast<const E*>(v_cache), sel, n_blocks, static_cast<const E*>(gate),
-      static_cast<E*>(out), part);
+  if constexpr (sizeof(E) == 2 && D == 128) {
+    attn_bf16_d128_kernel<G><<<grid, 64 * kWaves, 0, st>>>(
+        g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+        static_cast<const uint16_t*>(v_cache), sel, n_blocks, static_cast<const uint16_t*>(gate),
+        static_cast<uint16_t*>(out), part);
+  } else {
+    attn_split_kernel<E, G, D><<<grid, 64, 0, st>>>(
+        g, plan, static_cast<const E*>(q), static_cast<const E*>(k_cache),
+        static_cast<const E*>(v_cache), sel, n_blocks, static_cast<const E*>(gate),
+        static_cast<E*>(out), part);
+  }
   if (plan.n_splits > 1) {
-    attn_combine_kernel<E, G, D><<<g.T * g.Hkv, 256, 0, st>>>(
+    attn_combine_kernel<E, G, D, kMaxSplits><<<g.T * g.Hkv, 256, 0, st>>>(
         g, plan, part, static_cast<const E*>(gate), static_cast<E*>(out));
   }
   return hipGetLastError();
@@ -573,17 +997,26 @@ hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const voi
   }
 }
 
+template <typename E, int DI>
+void score_hd(const Geo& g, const void* qI, const float* w, const float* pooled,
+              float* scores, hipStream_t st) {
+  dim3 grid(g.T, (g.nbcap + 63) / 64);
+  const E* q = static_cast<const E*>(qI);
+  if (g.HI <= 4) {
+    score_kernel<E, 4, DI><<<grid, 64, 0, st>>>(g, q, w, pooled, scores);
+  } else if (g.HI <= 8) {
+    score_kernel<E, 8, DI><<<grid, 64, 0, st>>>(g, q, w, pooled, scores);
+  } else {
+    score_kernel<E, 16, DI><<<grid, 64, 0, st>>>(g, q, w, pooled, scores);
+  }
+}
+
 template <typename E>
 hipError_t score_h(const Geo& g, const void* qI, const float* w, const float* pooled,
                    float* scores, hipStream_t st) {
-  dim3 grid(g.T, (g.nbcap + 255) / 256);
-  if (g.HI <= 4) {
-    score_kernel<E, 4><<<grid, 64, 0, st>>>(g, static_cast<const E*>(qI), w, pooled, scores);
-  } else if (g.HI <= 8) {
-    score_kernel<E, 8><<<grid, 64, 0, st>>>(g, static_cast<const E*>(qI), w, pooled, scores);
-  } else {
-    score_kernel<E, 16><<<grid, 64, 0, st>>>(g, static_cast<const E*>(qI), w, pooled, scores);
-  }
+  if (g.dI == 32) score_hd<E, 32>(g, qI, w, pooled, scores, st);
+  else if (g.dI == 64) score_hd<E, 64>(g, qI, w, pooled, scores, st);
+  else score_hd<E, 128>(g, qI, w, pooled, scores, st);
   return hipGetLastError();
 }
 
@@ -630,9 +1063,10 @@ hipError_t launch_attend(const Geo& g, int elem, const AttnPlan& plan, const voi
                          const int32_t* n_blocks, const void* gate, void* out, float* part,
                          hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  return elem == kBF16
-             ? attend_g<uint16_t>(g, plan, q, k_cache, v_cache, sel, n_blocks, gate, out, part, st)
-             : attend_g<float>(g, plan, q, k_cache, v_cache, sel, n_blocks, gate, out, part, st);
+  return elem == kBF16 ? attend_g<uint16_t>(g, plan, q, k_cache, v_cache, sel, n_blocks, gate,
+                                            out, part, st)
+                       : attend_g<float>(g, plan, q, k_cache, v_cache, sel, n_blocks, gate, out,
+                                         part, st);
 }
 
 }  // namespace qsa

@@ -186,7 +186,7 @@ class DeviceCase:
         return {"out": torch.empty((T, sp.n_q_heads, sp.head_dim), dtype=self.dt, device=self.device),
                 "sel": torch.empty((T, k), dtype=torch.int32, device=self.device),
                 "n_blocks": torch.empty((T,), dtype=torch.int32, device=self.device),
-                "ws": torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=self.device)}
+                "ws": torch.zeros((max(ws_bytes, 16),), dtype=torch.uint8, device=self.device)}
 
     def forward(self, inp: dict, outs: dict, layer: int = 0, stream=None) -> None:
         st = self.layers[layer]

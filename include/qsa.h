@@ -116,7 +116,8 @@ int64_t qsa_pooled_ld(const qsa_params* params, const qsa_batch* batch);
 /* Bytes of scratch workspace any entry point may need for this call (same
  * value for every entry point; 0 when n_tokens == 0).  The workspace holds
  * block scores, split-attention partials and, when the caller does not ask
- * for them, the selections.  Its contents need no initialisation. */
+ * for them, the selections.  Its contents need no initialisation; calls that
+ * share one workspace must not overlap in time (same stream, or synchronised). */
 size_t qsa_workspace_size(const qsa_params* params, const qsa_batch* batch);
 
 /* Indexer-key append and incremental block pooling.

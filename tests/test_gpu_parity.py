@@ -210,7 +210,7 @@ def test_score_values_bitexact_and_side_cache_rows():
     k = dc.params.budget // dc.r
     sel = torch.empty((T, k), dtype=torch.int32, device="cuda")
     nbl = torch.empty((T,), dtype=torch.int32, device="cuda")
-    ws = torch.empty((qsa.qsa_workspace_size(dc.params, batch),), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((qsa.qsa_workspace_size(dc.params, batch),), dtype=torch.uint8, device="cuda")
     qsa.qsa_score_select(dc.params, batch, qI, w, st["pooled"], sel, nbl, scores, ws)
     torch.cuda.synchronize()
     from gpu_harness import dims_of
@@ -233,3 +233,25 @@ def test_zero_tokens_noop():
                     dc.layers[0]["k"], dc.layers[0]["v"], dc.layers[0]["kI"],
                     dc.layers[0]["pooled"], dummy)
     torch.cuda.synchronize()
+
+
+def test_repeated_attend_reuses_workspace():
+    """Repeated calls on one workspace (holding the previous call's split
+    partials) give bit-identical outputs: nothing carries over between calls,
+    for a plan with many splits (one decode token) and a multi-token call."""
+    for name, kw in (("decode_32k_bf16", {}), ("long_decode_256k_bf16", dict(ctx=20000, steps=1)),
+                     ("tiny_prefill_f32", dict(chunk=512))):
+        case = workloads.make_case(name, **kw)
+        dc = runner.DeviceCase(case)
+        inp = dc.call_inputs(0)
+        outs = dc.alloc_outputs(inp)
+        dc.forward(inp, outs)
+        torch.cuda.synchronize()
+        first = outs["out"].clone()
+        st = dc.layers[0]
+        for _ in range(3):
+            again = torch.empty_like(first)
+            qsa.qsa_attend(dc.params, inp["batch"], inp["q"], st["k"], st["v"], outs["sel"],
+                           outs["n_blocks"], inp["gate"], again, outs["ws"])
+            torch.cuda.synchronize()
+            assert torch.equal(again, first), name
