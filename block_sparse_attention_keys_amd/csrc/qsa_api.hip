@@ -36,6 +36,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kMfmaMinUnits = 512;  // (token, KV head) units that fill the chip without splits
 constexpr int kMaxK = 2048;
 
 struct Plan {
@@ -150,6 +151,13 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   splits = (tiles + waves * tpw - 1) / (waves * tpw);
   pl.attn.n_splits = (int32_t)splits;
   pl.attn.split_tokens = (int32_t)(64 * waves * tpw);
+  // Many (token, KV head) units, as in prefill: the MFMA kernel, one wave per
+  // unit.  Few units (decode): the split-list bandwidth kernel.
+  pl.attn.mfma = (pl.elem == qsa::kBF16 && g.D == 128 && units >= kMfmaMinUnits) ? 1 : 0;
+  if (pl.attn.mfma) {
+    pl.attn.n_splits = 1;
+    pl.attn.split_tokens = (int32_t)(64 * tiles);
+  }
 
   const int64_t T = b.n_tokens;
   size_t off = 0;

@@ -28,6 +28,7 @@ struct Geo {
 
 // Split-KV plan of the attention kernels.
 struct AttnPlan {
+  int32_t mfma;          // 1: prefill MFMA kernel (one wave per unit, no splits)
   int32_t n_splits;      // splits per (token, KV head), <= kPlanMaxSplits
   int32_t split_tokens;  // tokens of the selection list per split (multiple of 64 * waves)
 };

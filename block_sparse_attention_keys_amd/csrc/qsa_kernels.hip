@@ -30,6 +30,8 @@ namespace qsa {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(4))) const uint32_t CU32;  // constant (scalar) memory
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -953,10 +955,223 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill attention on MFMA (bf16, D = 128): one wave per (token, KV head)
+// unit, 4 units per workgroup, no splits (prefill has units to spare).
+// Matrix-core layout of v_mfma_f32_16x16x32_bf16 (64 lanes, l = lane):
+//   A[i][k]: i = l%16, k = 8*(l/16) + e;  B[k][j]: j = l%16, k = 8*(l/16) + e;
+//   C[i][j]: j = l%16, i = 4*(l/16) + r.
+// Per 64-key tile of the unit's selection list:
+//   S[head][key] = sum over 4 k-steps of Q (A: heads padded to 16 rows, fixed
+//                  per unit, in registers) x K^T (B: 16 B of a cache row per
+//                  lane, straight from memory): 4 key tiles x 4 = 16 MFMAs;
+//   online softmax in base 2 on the accumulator layout (a head's 64 keys sit
+//                  in 16 lanes x 4 tiles: in-lane max, then 4 DPP steps);
+//   P (bf16) -> LDS [head][key], read back as the A operand;
+//   V -> LDS transposed [dim][key] (4 keys packed per 8-byte store), read as
+//                  the B operand: O[head][dim] += P x V, 8 dim tiles x 2 k-steps.
+// LDS rows are padded to 136 B, which keeps the 16-lane B reads conflict-free.
+template <int G>
+__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
+    Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
+    uint16_t* __restrict__ out) {
+  static_assert(G <= 16, "heads per KV head must fit the 16 MFMA rows");
+  constexpr int D = 128;
+  constexpr int RS = 136;                 // LDS row stride (bytes) of VT and P
+  constexpr int RND = 128;                // list positions resolved per round
+  __shared__ __attribute__((aligned(16))) unsigned char VT_all[kWaves][D * RS];
+  __shared__ __attribute__((aligned(16))) unsigned char P_all[kWaves][16 * RS];
+  __shared__ int32_t rows_all[kWaves][RND];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * kWaves + wid;
+  if (unit >= g.T * g.Hkv) return;  // whole wave; only wave-level sync below
+  unsigned char* VT = VT_all[wid];
+  unsigned char* Pl = P_all[wid];
+  int32_t* rows = rows_all[wid];
+  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
+  const QueryPos qp = query_pos(g, t);
+  if (!qp.ok) return;
+  const ListInfo L = list_info(g, qp, nblk, t);
+  const int32_t* srow = sel + (int64_t)t * g.k;
+  const int h0 = kvh * G;
+  const int c16 = lane & 15, grp = lane >> 4;
+
+  // Q as the A operand: row c16 = head (zero past G), k = dims 32 ks + 8 grp + e.
+  bf16x8_t qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 w = make_uint4(0u, 0u, 0u, 0u);
+    if (c16 < G)
+      w = *reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0 + c16) * D + 32 * ks + 8 * grp);
+    qa[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  float m[4], ls[4];
+  f32x4_t O[8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m[r] = -INFINITY;
+    ls[r] = 0.0f;
+  }
+#pragma unroll
+  for (int n = 0; n < 8; ++n) O[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  for (int r0 = 0; r0 < L.n_list; r0 += RND) {
+    // Resolve this round's cache rows (4 independent chains per lane).
+#pragma unroll
+    for (int e = 0; e < RND / 64; ++e) {
+      const int i = r0 + 64 * e + lane;
+      int32_t rv = -1;
+      if (i < L.n_list) {
+        const int s = list_token(g, L, srow, i);
+        const int64_t rr = (s >= 0 && s <= qp.p) ? kv_row(g, qp.b, kvh, s) : -1;
+        rv = rr >= 0 ? (int32_t)(rr / D) : -1;
+      }
+      rows[64 * e + lane] = rv;
+    }
+    wave_sync();
+    const int r1 = min(r0 + RND, L.n_list);
+    for (int it = r0; it < r1; it += 64) {
+      const int32_t* tr = rows + (it - r0);
+      // K as the B operand: key tile n, k-step ks -> 16 B of row (16n + c16).
+      uint4 kb[4][4];
+      int32_t krow[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        krow[n] = tr[16 * n + c16];
+        const int64_t base = (int64_t)(krow[n] >= 0 ? krow[n] : 0) * D + 8 * grp;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kb[n][ks] = *reinterpret_cast<const uint4*>(kc + base + 32 * ks);
+      }
+      // S = Q K^T
+      f32x4_t S[4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        S[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          S[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              qa[ks], __builtin_bit_cast(bf16x8_t, kb[n][ks]), S[n], 0, 0, 0);
+      }
+      // V rows 4*c16 + s, chunks grp + 4 j (8 dims each).
+      uint4 vv[4][4];
+#pragma unroll
+      for (int sft = 0; sft < 4; ++sft) {
+        const int32_t rv = tr[4 * c16 + sft];
+        const bool ok = rv >= 0;
+        const int64_t base = (int64_t)(ok ? rv : 0) * D;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint4 w = *reinterpret_cast<const uint4*>(vc + base + 8 * (grp + 4 * j));
+          vv[j][sft] = ok ? w : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      // Online softmax: lane rows r -> head 4 grp + r; keys 16n + c16.
+      float alpha[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const float z = krow[n] >= 0 ? S[n][r] * g.attn_scale_log2 : -INFINITY;
+          S[n][r] = z;
+          mx = fmaxf(mx, z);
+        }
+        mx = fmaxf(mx, dpp<0xB1>(mx));
+        mx = fmaxf(mx, dpp<0x4E>(mx));
+        mx = fmaxf(mx, dpp<0x141>(mx));
+        mx = fmaxf(mx, dpp<0x140>(mx));
+        const float mn = fmaxf(m[r], mx);
+        alpha[r] = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - mn);
+        m[r] = mn;
+        float lsum = 0.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+          const float z = S[n][r];
+          const uint16_t pb = (z == -INFINITY) ? (uint16_t)0 : bf16_rne(exp2f(z - mn));
+          lsum += to_f32(pb);
+          reinterpret_cast<uint16_t*>(Pl + (4 * grp + r) * RS)[16 * n + c16] = pb;
+        }
+        ls[r] = fmaf(ls[r], alpha[r], lsum);
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O[n][r] *= alpha[r];
+      }
+      // V^T -> LDS: for dim 8 c + e, keys 4 c16 .. 4 c16 + 3 as one 8-byte store.
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = grp + 4 * j;
+        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[j][0]);
+        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[j][1]);
+        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[j][2]);
+        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[j][3]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sl = (e & 1) ? 0x07060302u : 0x05040100u;
+          uint2 pk;
+          pk.x = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sl);
+          pk.y = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sl);
+          *reinterpret_cast<uint2*>(VT + (8 * c + e) * RS + 8 * c16) = pk;
+        }
+      }
+      wave_sync();
+      // O += P V
+      bf16x8_t pa[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pa[ks] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(Pl + c16 * RS + 64 * ks + 16 * grp));
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const uint4 vb =
+              *reinterpret_cast<const uint4*>(VT + (16 * n + c16) * RS + 64 * ks + 16 * grp);
+          O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks], __builtin_bit_cast(bf16x8_t, vb),
+                                                         O[n], 0, 0, 0);
+        }
+      }
+      wave_sync();
+    }
+    wave_sync();
+  }
+  // Denominators: the 16 lanes of a row group hold partial sums of the same heads.
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float l = ls[r];
+    l += dpp<0xB1>(l);
+    l += dpp<0x4E>(l);
+    l += dpp<0x141>(l);
+    l += dpp<0x140>(l);
+    const int h = 4 * grp + r;
+    if (h >= G) continue;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int64_t idx = ((int64_t)t * g.Hq + h0 + h) * D + 16 * n + c16;
+      const float sg = 1.0f / (1.0f + expf(-to_f32(gate[idx])));
+      out[idx] = bf16_rne(O[n][r] * inv * sg);
+    }
+  }
+}
+
 template <typename E, int G, int D>
 hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* sel, const int32_t* n_blocks,
                        const void* gate, void* out, float* part, hipStream_t st) {
+  if constexpr (sizeof(E) == 2 && D == 128) {
+    if (plan.mfma) {
+      attn_prefill_mfma_kernel<G><<<(g.T * g.Hkv + kWaves - 1) / kWaves, 64 * kWaves, 0, st>>>(
+          g, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+          static_cast<const uint16_t*>(v_cache), sel, n_blocks,
+          static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out));
+      return hipGetLastError();
+    }
+  }
   dim3 grid(g.T * g.Hkv, plan.n_splits);
   if constexpr (sizeof(E) == 2 && D == 128) {
     attn_bf16_d128_kernel<G><<<grid, 64 * kWaves, 0, st>>>(
