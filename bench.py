@@ -44,7 +44,23 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="cache copies to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB megabytes (counter calibration)")
     return ap.parse_args()
+
+
+def calibrate_copy(mb: int) -> None:
+    """A plain device-to-device copy of a known size, 5 times: what the HBM
+    counters read for it scales their readings of the QSA kernels."""
+    import torch
+    n = mb * 1000 * 1000
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
 
 
 def log(*a):
@@ -53,6 +69,9 @@ def log(*a):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the QSA hot path "
@@ -69,9 +88,7 @@ def main():
     name = args.workload
     sp = workloads.SPECS[name]
     if sp.kind != "decode":
-        print(json.dumps({"error": "bench.py times the decode workloads; prefill is measured by "
-                                   "the parity runs", "workload": name}))
-        sys.exit(2)
+        return bench_prefill(args, name)
 
     t0 = time.time()
     case = workloads.make_case(name, seed=0)
@@ -170,7 +187,9 @@ def main():
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tok/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; contexts U[8192,131072]; N(0,1)/sqrt(d) q/k/v)",
+        "data": ("synthetic (seeded; " + (f"contexts U[{sp.ctx_lo},{sp.ctx_hi}]" if sp.ctx_hi
+                                          else f"context {sp.ctx}") +
+                 "; N(0,1)/sqrt(d) q/k/v; decode inputs drawn on the GPU)"),
         "config": {"workload": name, "batch": B, "ctx_min": min(case.ctx),
                    "ctx_max": max(case.ctx), "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "block_size": r, "budget": sp.budget,
@@ -183,12 +202,125 @@ def main():
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "avg_launch_us": round(attn_ms * 1e3, 2), "bytes_per_launch": attn_bytes,
-                     "traffic": None},
+                     "traffic": counter_traffic(f"attn_{name}_hbm_counters.txt")},
     }
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, sp, args.cpu_seconds)
     print(json.dumps(res), flush=True)
+
+
+def counter_traffic(summary_name):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel
+    source has changed since the counters were taken."""
+    from block_sparse_attention_keys_amd import profiling
+    s = profiling.read_summary(os.path.join(ROOT, "profiles", summary_name))
+    if not s or s.get("kernel_source_sha256") != profiling.kernel_source_sha256():
+        return None
+    return int(float(s["traffic_bytes_per_launch"]))
+
+
+def bench_prefill(args, name):
+    """Chunked prefill of one sequence: a step is every chunk call of the
+    workload in order (append, pool, score, select, attend per chunk).  The
+    value is selected attention FLOP/s (4 D Hq per selected key per token)."""
+    import torch
+    from block_sparse_attention_keys_amd import qsa, runner, workloads
+    sp = workloads.SPECS[name]
+    case = workloads.make_case(name, seed=0)
+    dc = runner.DeviceCase(case)
+    calls = [dc.call_inputs(i) for i in range(len(case.calls))]
+    outs = [dc.alloc_outputs(x) for x in calls]
+    r, k = sp.block_size, sp.k_blocks
+    flops = []
+    for x in calls:
+        s0, e0 = x["spans"][0]
+        n = np.arange(s0, e0) + 1
+        nb = n // r
+        nsel = r * np.minimum(k, nb) + (n - r * nb)
+        flops.append(float((nsel * sp.n_q_heads * 4 * sp.head_dim).sum()))
+    total_flops = sum(flops)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for x, o in zip(calls, outs):
+            dc.forward(x, o)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    # dominant kernel: the attention of each chunk call, alone, bracketed by events
+    st = dc.layers[0]
+    ev = []
+    for x, o in zip(calls, outs):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        qsa.qsa_attend(dc.params, x["batch"], x["q"], st["k"], st["v"], o["sel"], o["n_blocks"],
+                       x["gate"], o["out"], o["ws"])
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_tflops = total_flops / (sum(attn_ms) * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(total_flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (selected blocks, whole prefill step)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1)/sqrt(d); planted blocks at 1% density)",
+        "config": {"workload": name, "tokens": sp.prefill_len, "chunk": sp.chunk,
+                   "n_q_heads": sp.n_q_heads, "n_kv_heads": sp.n_kv_heads,
+                   "head_dim": sp.head_dim, "block_size": r, "budget": sp.budget},
+        "selected_gflop_per_step": round(total_flops / 1e9, 2),
+        "roofline": {"bound": "mfma", "kernel": "prefill attention (qsa_attend, bf16 MFMA)",
+                     "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "avg_launch_us": round(float(np.mean(attn_ms)) * 1e3, 1),
+                     "flops_per_launch": round(total_flops / len(calls)), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(case, sp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_prefill(case, sp, seconds):
+    """The CPU oracle on query tokens of the last chunk (evenly spaced),
+    repeated until about `seconds` of wall time; selected TFLOP/s."""
+    import oracle
+    from block_sparse_attention_keys_amd import workloads
+    orc = oracle.load()
+    dims = dict(n_q_heads=sp.n_q_heads, n_kv_heads=sp.n_kv_heads, head_dim=sp.head_dim,
+                n_idx_heads=sp.n_idx_heads, idx_dim=sp.idx_dim, block_size=sp.block_size,
+                budget=sp.budget, attn_scale=0.0, idx_scale=0.0)
+    K, V, kI = (workloads.as_f32(case.k[0]), workloads.as_f32(case.v[0]),
+                workloads.as_f32(case.kI[0]))
+    n_tok = K.shape[0]
+    pos = np.linspace(n_tok - sp.chunk, n_tok - 1, 64).astype(np.int64)
+    r, k = sp.block_size, sp.k_blocks
+    n = pos + 1
+    nb = n // r
+    flops = float(((r * np.minimum(k, nb) + n - r * nb) * sp.n_q_heads * 4 * sp.head_dim).sum())
+    reps = 0
+    t0 = time.time()
+    while True:
+        orc.sequence(dims, K, V, kI, pos, case.q[0][pos], case.qI[0][pos], case.w[0][pos],
+                     case.gate[0][pos])
+        reps += 1
+        if time.time() - t0 >= seconds:
+            break
+    dt = time.time() - t0
+    return {"value": round(reps * flops / dt / 1e12, 5), "unit": "TFLOP/s (selected blocks)",
+            "cores": orc.threads(), "kind": "oracle",
+            "sample": f"{reps} x 64 query tokens of the last 4096-token chunk (OpenMP over "
+                      f"queries), {dt:.1f}s wall", "cpu_model": _cpu_model()}
 
 
 def cpu_baseline(case, sp, seconds):
