@@ -137,27 +137,25 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   g.past_len = b.past_len;
   g.page_table = b.page_table;
 
-  // Split-KV plan: about 2048 waves in flight (8 per CU); each wave walks
-  // tpw 64-token tiles; a split is one workgroup of `waves` waves.
+  // Split-KV plan.  A unit's list is cut into n_splits ranges of whole
+  // 64-token tiles that differ by at most one tile.  The 4-wave decode kernel
+  // aims at 512 workgroups (two per CU) with at least two tiles per split;
+  // the one-wave generic kernel at 2048 waves.
   const int64_t max_list = r ? std::min<int64_t>(b.max_kv_len, (int64_t)k * r + r - 1)
                              : (int64_t)b.max_kv_len;
   const int64_t tiles = std::max<int64_t>(1, (max_list + 63) / 64);
   const int64_t units = std::max<int64_t>(1, (int64_t)b.n_tokens * g.Hkv);
   const int64_t waves = qsa::attend_waves(pl.elem, g.D);
-  const int64_t max_splits = std::max<int64_t>(1, (tiles + waves - 1) / waves);
-  int64_t splits = std::max<int64_t>(1, (2048 + units * waves - 1) / (units * waves));
-  splits = std::min<int64_t>(std::min<int64_t>(splits, max_splits), qsa::kPlanMaxSplits);
-  const int64_t tpw = (tiles + splits * waves - 1) / (splits * waves);
-  splits = (tiles + waves * tpw - 1) / (waves * tpw);
+  int64_t splits = waves > 1 ? std::min((512 + units - 1) / units, (tiles + 1) / 2)
+                             : std::min((2048 + units - 1) / units, tiles);
+  splits = std::max<int64_t>(1, std::min<int64_t>(splits, qsa::kPlanMaxSplits));
   pl.attn.n_splits = (int32_t)splits;
-  pl.attn.split_tokens = (int32_t)(64 * waves * tpw);
+  pl.attn.tiles = (int32_t)tiles;
   // Many (token, KV head) units, as in prefill: the MFMA kernel, one wave per
-  // unit.  Few units (decode): the split-list bandwidth kernel.
+  // unit.  Few units (decode): the split-list bandwidth kernels.
   pl.attn.mfma = (pl.elem == qsa::kBF16 && g.D == 128 && units >= kMfmaMinUnits) ? 1 : 0;
-  if (pl.attn.mfma) {
-    pl.attn.n_splits = 1;
-    pl.attn.split_tokens = (int32_t)(64 * tiles);
-  }
+  if (pl.attn.mfma) pl.attn.n_splits = 1;
+  splits = pl.attn.n_splits;
 
   const int64_t T = b.n_tokens;
   size_t off = 0;

@@ -30,7 +30,7 @@ struct Geo {
 struct AttnPlan {
   int32_t mfma;          // 1: prefill MFMA kernel (one wave per unit, no splits)
   int32_t n_splits;      // splits per (token, KV head), <= kPlanMaxSplits
-  int32_t split_tokens;  // tokens of the selection list per split (multiple of 64 * waves)
+  int32_t tiles;         // 64-token tiles of the longest selection list
 };
 constexpr int kPlanMaxSplits = 128;
 

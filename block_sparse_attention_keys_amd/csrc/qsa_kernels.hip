@@ -32,6 +32,8 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(4))) const uint32_t CU32;  // constant (scalar) memory
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
@@ -494,71 +496,82 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// A split covers the 64-token tiles [tiles * s / S, tiles * (s + 1) / S) of the
+// longest list (S = n_splits): the same boundaries for every unit, so splits
+// differ by at most one tile.
+__device__ __forceinline__ int split_begin(const AttnPlan& plan, int split) {
+  return 64 * (int)(((int64_t)split * plan.tiles) / plan.n_splits);
+}
+
 // Split merge: one workgroup per (token, KV head) unit, launched after the
 // attention kernel (the kernel boundary makes every split's partial visible).
 // Partials: [split][G][D] o, then [G] m, then [G] l (base-2 log-sum-exp
-// state).  The (m, l) of all splits are staged in LDS first, so the o loads of
-// all splits are independent and in flight together; then the sigmoid gate.
-template <typename E, int G, int D, int MAXS>
+// state); a unit whose query lies outside the capacities has l = -1 in every
+// split and is skipped.  The gate and the partials of kCombineBatch splits are
+// loaded together and merged under a running maximum: one memory round trip
+// per batch of splits.
+constexpr int kCombineBatch = 16;
+template <typename E, int G, int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(Geo g, AttnPlan plan,
                                                            const float* __restrict__ part,
                                                            const E* __restrict__ gate,
                                                            E* __restrict__ out) {
   constexpr int NT = 256;
   constexpr int SP = G * (D + 2);
-  __shared__ float wgt[MAXS * G];   // m, then the split weight
-  __shared__ float lsp[MAXS * G];   // l
-  __shared__ float Linv[G];
-  const int unit = blockIdx.x, tid = threadIdx.x;
-  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv, h0 = kvh * G;
-  const QueryPos qp = query_pos(g, t);
-  if (!qp.ok) return;
-  const int n_splits = plan.n_splits;
-  const float* P0 = part + (int64_t)unit * n_splits * SP;
-  for (int e = tid; e < n_splits * G; e += NT) {
-    const int sp = e / G, h = e - sp * G;
-    wgt[e] = P0[(int64_t)sp * SP + G * D + h];
-    lsp[e] = P0[(int64_t)sp * SP + G * D + G + h];
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < n_splits; ++sp) M = fmaxf(M, wgt[sp * G + tid]);
-    float L = 0.0f;
-    for (int sp = 0; sp < n_splits; ++sp) {
-      const float m = wgt[sp * G + tid];
-      const float w = (m == -INFINITY) ? 0.0f : exp2f(m - M);
-      wgt[sp * G + tid] = w;
-      L = fmaf(lsp[sp * G + tid], w, L);
-    }
-    Linv[tid] = L > 0.0f ? 1.0f / L : 0.0f;
-  }
-  __syncthreads();
   constexpr int EPT = (G * D >= NT) ? G * D / NT : 1;  // elements per thread, inside one head
   static_assert(D % EPT == 0, "combine layout");
-  const int e0 = tid * EPT, h = e0 / D, d0 = e0 - h * D;
+  const int unit = blockIdx.x;
+  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
+  const int e0 = threadIdx.x * EPT;
   if (e0 >= G * D) return;
-  float O[EPT];
+  const int h = e0 / D, d0 = e0 - h * D;
+  const int64_t ob = ((int64_t)t * g.Hq + kvh * G + h) * D + d0;
+  float gt[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) gt[i] = to_f32(gate[ob + i]);
+  const int S = plan.n_splits;
+  const float* P0 = part + (int64_t)unit * S * SP;
+  const float flag = P0[G * D + G];
+  float M = -INFINITY, Ls = 0.0f, O[EPT];
 #pragma unroll
   for (int i = 0; i < EPT; ++i) O[i] = 0.0f;
-#pragma unroll 4
-  for (int sp = 0; sp < n_splits; ++sp) {
-    const float w = wgt[sp * G + h];
-    const float* src = P0 + (int64_t)sp * SP + h * D + d0;
+  for (int s0 = 0; s0 < S; s0 += kCombineBatch) {
+    float mv[kCombineBatch], lv[kCombineBatch], ov[kCombineBatch][EPT];
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) O[i] = fmaf(src[i], w, O[i]);
+    for (int c = 0; c < kCombineBatch; ++c) {
+      const float* ps = P0 + (int64_t)min(s0 + c, S - 1) * SP;
+      mv[c] = ps[G * D + h];
+      lv[c] = ps[G * D + G + h];
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) ov[c][i] = ps[h * D + d0 + i];
+    }
+    float cm = M;
+#pragma unroll
+    for (int c = 0; c < kCombineBatch; ++c)
+      if (s0 + c < S) cm = fmaxf(cm, mv[c]);
+    const float a = (M == -INFINITY) ? 0.0f : exp2f(M - cm);
+    Ls *= a;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) O[i] *= a;
+#pragma unroll
+    for (int c = 0; c < kCombineBatch; ++c) {
+      const float w = (s0 + c < S && mv[c] != -INFINITY) ? exp2f(mv[c] - cm) : 0.0f;
+      Ls = fmaf(lv[c], w, Ls);
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) O[i] = fmaf(ov[c][i], w, O[i]);
+    }
+    M = cm;
   }
-  const float inv = Linv[h];
+  if (flag < 0.0f) return;
+  const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const int64_t idx = ((int64_t)t * g.Hq + h0 + h) * D + d0 + i;
-    const float sg = 1.0f / (1.0f + expf(-to_f32(gate[idx])));
-    out[idx] = from_f32<E>(O[i] * inv * sg);
+    const float sg = 1.0f / (1.0f + expf(-gt[i]));
+    out[ob + i] = from_f32<E>(O[i] * inv * sg);
   }
 }
 
 constexpr int kWaves = 4;       // waves per workgroup of the bf16 D=128 kernel
-constexpr int kMaxSplits = 128;  // splits per unit (bounded by the host plan)
 
 template <typename E, int G, int D>
 __global__ __launch_bounds__(64) void attn_split_kernel(
@@ -577,8 +590,8 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
   const QueryPos qp = query_pos(g, t);
   const ListInfo L = list_info(g, qp, nblk, t);
-  const int i0 = split * plan.split_tokens;
-  const int i1 = min(i0 + plan.split_tokens, L.n_list);
+  const int i0 = split_begin(plan, split);
+  const int i1 = min(split_begin(plan, split + 1), L.n_list);
   const int h0 = kvh * G;
 
   float m[G], l[G], o[G][DPL];
@@ -708,212 +721,341 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       P[G * D + h] = m[h];
-      P[G * D + G + h] = l[h];
+      P[G * D + G + h] = qp.ok ? l[h] : -1.0f;  // -1: the query lies outside the capacities
     }
   }
 }
 
-// bf16, D = 128: the decode-bandwidth kernel.  A workgroup of 4 waves owns one
-// split of one (token, KV head) unit; its waves take the split's 64-token
-// tiles in turn.  Per tile, in one wave:
-//   1. each lane holds the cache row of one token (resolved one tile ahead,
-//      while the previous tile's loads are in flight);
-//   2. K and V of the tile are loaded up front in 16-byte chunks, 4 rows per
-//      instruction (fully coalesced): lane l holds chunk l%16 of the tokens
-//      l/16 + 4j, j = 0..15;
-//   3. K goes through padded LDS so that QK runs lane-per-token, as bf16 dot2
-//      against the query, which sits in scalar registers;
-//   4. online softmax in base 2, one max per head per tile;
-//   5. V stays in registers: each lane accumulates its 8 dims for its 16
-//      tokens, pairing tokens for bf16 dot2 with the probabilities rounded to
-//      bf16 (the denominator sums the same rounded values).
-// The 4 waves merge in LDS; a unit with several splits writes one partial per
-// split, merged by attn_combine_kernel.
-template <int G>
-__global__ __launch_bounds__(256) void attn_bf16_d128_kernel(
+// Buffer resource over [base, base + bytes): loads at or past the end return
+// zeros (raw buffer, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr uint32_t kOobOffset = 0xFFFFF000u;  // past the end of every buffer that uses it
+constexpr int kStreamPolicy = 2;              // non-temporal: each K/V row is read once
+
+// bf16, D = 128 decode kernel.  A workgroup of 4 waves owns one split of one
+// (token, KV head) unit; its waves take the split's 64-token tiles in turn.
+// Turning list positions into cache rows takes dependent loads (sequence and
+// selection entry; position and page; row), so the loads that do not depend
+// on each other go out together: the query, n_blocks, the selection entries
+// and the sequence search first; then the position and the page-table entries
+// of the selected blocks (the tail's pages follow once the position is known).
+// Per 64-token tile, in one wave:
+//   QK on the matrix cores: S[token][head] = K (A operand: 16 B of a cache row
+//     per lane, straight from memory) x Q^T (B operand: the query from LDS,
+//     heads padded to 16 columns): 4 token groups x 4 dim steps =
+//     16 v_mfma_f32_16x16x32_bf16;
+//   online softmax in base 2 on the accumulator layout (a lane holds one head
+//     for 16 tokens: in-lane max, then two cross-row exchanges); p rounded to
+//     bf16 (the denominator sums the same rounded values) and staged in LDS as
+//     token pairs;
+//   PV on the vector ALU: a lane holds 4 dims of 32 tokens of V (8-byte
+//     chunks, two full rows per load instruction) and accumulates bf16 dot2
+//     over token pairs, the p pairs read from LDS as broadcasts.
+// The next tile's K is loaded right after this tile's QK and its V right after
+// this tile's PV, so each wave keeps a tile of loads in flight while it
+// computes.  The loads are unconditional (a wave's last look-ahead reads
+// nothing useful): conditional loads would keep two copies of the tile
+// registers alive.  With BUF (caches under 4 GiB) K and V go through buffer
+// resources: masked rows and the last look-ahead read past the end and come
+// back zero, without memory traffic.  Otherwise they read row 0 and masked V
+// rows are zeroed in registers.  The 4 waves merge in LDS; a unit with several
+// splits writes one partial per split, merged by attn_combine_kernel.
+template <int G, bool BUF>
+__global__ __launch_bounds__(256) void attn_decode_kernel(
     Geo g, AttnPlan plan, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
-    uint16_t* __restrict__ out, float* __restrict__ part) {
+    uint16_t* __restrict__ out, float* __restrict__ part, uint32_t kv_bytes) {
+  static_assert(G >= 1 && G <= 16 && 16 % G == 0, "heads per KV head must divide 16");
   constexpr int D = 128;
-  constexpr int KS = 272;  // LDS row stride in bytes: 256 + 16 keeps ds_read_b128 conflict-free
-  constexpr int RR = 1024;  // rows resolved per round (4 tiles per wave)
-  __shared__ __attribute__((aligned(16))) unsigned char Ks_all[kWaves][64 * KS];
-  __shared__ int32_t rowidx[RR];                   // cache row (element offset / D), -1 = masked
-  __shared__ uint32_t PP_all[kWaves][4 * 8 * G];  // bf16 pairs of p: [token group][pair][head]
+  constexpr int RR = 1024;       // list positions resolved per round
+  constexpr int EPR = RR / 256;  // positions per thread per round
+  __shared__ int32_t rowidx[RR];                // cache row index, -1 = masked
+  __shared__ uint32_t PP_all[kWaves][32 * G];   // p as bf16 pairs: [token pair][head]
+  __shared__ uint4 qs[16][17];                  // query: [head, padded to 16][16-byte chunk]
+  __shared__ __attribute__((aligned(16))) float wo_all[kWaves][G * D];
   __shared__ float wm[kWaves][G], wl[kWaves][G];
 
-  const int unit = blockIdx.x, split = blockIdx.y;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  unsigned char* Ks = Ks_all[wid];
+  const int unit = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int c16 = lane & 15, q4 = lane >> 4;    // MFMA column, lane row group
+  const int half = lane >> 5, c32 = lane & 31;  // PV: token half, 4-dim chunk
   uint32_t* PP = PP_all[wid];
-  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
-  const QueryPos qp = query_pos(g, t);
-  const ListInfo L = list_info(g, qp, nblk, t);
-  const int i0 = split * plan.split_tokens;
-  const int i1 = min(i0 + plan.split_tokens, L.n_list);
-  const int h0 = kvh * G;
-  const int grp = lane >> 4, cq = lane & 15;
-  const uint4* qv = reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0) * D);
+  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv, h0 = kvh * G;
   const int32_t* srow = sel + (int64_t)t * g.k;
+  const int i0 = split_begin(plan, split), i_end = split_begin(plan, split + 1);
+  const int sel_end = g.r > 0 ? (g.k << g.log2r) : 0;  // list positions that come from sel
+  const int cap_blocks = g.r > 0 ? (g.cap >> g.log2r) : 0;
 
-  auto resolve = [&](int i) -> int32_t {
-    if (i >= i1) return -1;
-    const int s = list_token(g, L, srow, i);
-    const int64_t r = (s >= 0 && s <= qp.p) ? kv_row(g, qp.b, kvh, s) : -1;
-    return r >= 0 ? (int32_t)(r / D) : -1;
-  };
-
-  float m[G], ls[G], o[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    ls[h] = 0.0f;
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[h][d] = 0.0f;
+  // Step 1 of the row resolution (independent loads).
+  {
+    const int hq = tid >> 4, ch = tid & 15;
+    qs[hq][ch] = hq < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0 + hq) * D +
+                                                          8 * ch)
+                        : make_uint4(0u, 0u, 0u, 0u);
   }
-
-  // The split is walked in rounds of RR list positions: first the whole
-  // round's cache rows are resolved into LDS (selection entry, then page
-  // table: two dependent loads, paid once per round), then the waves take the
-  // round's 64-token tiles in turn.
-  for (int r0 = i0; r0 < i1; r0 += RR) {
-    __syncthreads();  // the previous round's rows are no longer read
-    for (int e = threadIdx.x; e < RR; e += 64 * kWaves) rowidx[e] = resolve(r0 + e);
-    __syncthreads();
-    const int r1 = min(r0 + RR, i1);
-  for (int it = r0 + 64 * wid; it < r1; it += 64 * kWaves) {
-    const int32_t* rows = rowidx + (it - r0);
-    const int32_t row = rows[lane];
-    // Full tiles (the common case) load unconditionally; a tile with an
-    // invalid row clamps its address to row 0 and zeroes what it loaded, so a
-    // masked token contributes exactly 0 even if row 0 holds NaN.
-    const bool full = __all(row >= 0);
-    uint4 vr[16];
-    {
-      uint4 kr[16];
-      int64_t ra[16];
+  const int nk_raw = g.r > 0 ? nblk[t] : 0;
+  int32_t sv[EPR], pg[EPR];
+  auto fetch_sel = [&](int r0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int32_t rj = rows[grp + 4 * j];
-        ra[j] = rj >= 0 ? (int64_t)rj * D : 0;
-      }
+    for (int j = 0; j < EPR; ++j) {
+      const int i = r0 + tid + 256 * j;
+      sv[j] = (i < sel_end) ? srow[i >> g.log2r] : -1;
+    }
+  };
+  fetch_sel(i0);
+  const int b = seq_of(g.cu_q, g.B, t);
+  // Token of position i if it lies in the selected part of the list, else -1.
+  auto spec_token = [&](int i, int blk) -> int {
+    if (g.r == 0) return i < g.cap ? i : -1;
+    return (i < sel_end && blk >= 0 && blk < cap_blocks) ? (blk << g.log2r) + (i & (g.r - 1))
+                                                         : -1;
+  };
+  auto fetch_pages = [&](int r0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) kr[j] = *reinterpret_cast<const uint4*>(kc + ra[j] + cq * 8);
+    for (int j = 0; j < EPR; ++j) {
+      const int s = spec_token(r0 + tid + 256 * j, sv[j]);
+      pg[j] = (g.page_table != nullptr && s >= 0)
+                  ? g.page_table[(int64_t)b * g.max_pages + (s >> g.log2ps)]
+                  : -1;
+    }
+  };
+  // Step 2: the position and the speculative pages.
+  const int past = g.past_len[b], cu_b = g.cu_q[b];
+  fetch_pages(i0);
+  const int p = past + (t - cu_b);
+  const bool ok = p >= 0 && p < g.cap;
+  ListInfo L = {0, 0, 0, 0};
+  if (ok) {
+    const int n = p + 1;
+    if (g.r == 0) {
+      L.n_list = n;
+    } else {
+      L.nb = n >> g.log2r;
+      const int nk = max(0, min(nk_raw, min(g.k, L.nb)));
+      L.nsel_tok = nk << g.log2r;
+      L.tail0 = L.nb << g.log2r;
+      L.n_list = L.nsel_tok + (n - L.tail0);
+    }
+  }
+  const int i1 = min(i_end, L.n_list);
+  // Step 3: rows (tail pages looked up now).
+  auto resolve_round = [&](int r0) {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) vr[j] = *reinterpret_cast<const uint4*>(vc + ra[j] + cq * 8);
-      if (!full) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          if (rows[grp + 4 * j] < 0) {
-            kr[j] = make_uint4(0u, 0u, 0u, 0u);
-            vr[j] = make_uint4(0u, 0u, 0u, 0u);
+    for (int j = 0; j < EPR; ++j) {
+      const int e = tid + 256 * j, i = r0 + e;
+      int s = -1;
+      bool spec = false;
+      if (i < i1) {
+        if (g.r == 0) {
+          s = i;
+          spec = true;
+        } else if (i < L.nsel_tok) {
+          const int blk = sv[j];
+          if (blk >= 0 && blk < L.nb) {
+            s = (blk << g.log2r) + (i & (g.r - 1));
+            spec = true;
           }
+        } else {
+          s = L.tail0 + (i - L.nsel_tok);
         }
       }
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        *reinterpret_cast<uint4*>(Ks + (grp + 4 * j) * KS + cq * 16) = kr[j];
+      int32_t row = -1;
+      if (s >= 0 && s <= p) {
+        if (g.page_table == nullptr) {
+          row = (int32_t)((int64_t)(b * g.Hkv + kvh) * g.cap + s);
+        } else {
+          const int page = spec ? pg[j] : g.page_table[(int64_t)b * g.max_pages + (s >> g.log2ps)];
+          if (page >= 0 && page < g.n_pages)
+            row = (int32_t)(((int64_t)page * g.Hkv + kvh) * g.page_size + (s & (g.page_size - 1)));
+        }
+      }
+      rowidx[e] = row;
     }
-    wave_sync();
+  };
 
-    float z[G];
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kc, kv_bytes), vrs = buffer_rsrc(vc, kv_bytes);
+  float m = -INFINITY, lp = 0.0f;  // this lane's head (c16): running max, partial denominator
+  float o[G][4];
 #pragma unroll
-    for (int h = 0; h < G; ++h) z[h] = 0.0f;
-    const unsigned char* krow = Ks + lane * KS;
-    // Kept rolled (2 chunks per trip): each trip holds 2 x 4G query words in
-    // SGPRs; a full unroll would hoist all 64G words and spill.
-#pragma unroll 2
-    for (int c = 0; c < 16; ++c) {
-      const uint4 kk = *reinterpret_cast<const uint4*>(krow + c * 16);
-      // The query is wave-uniform: read it through the constant address
-      // space (scalar loads into SGPRs, the dot2's scalar operand).  The
-      // opaque pointer keeps each chunk's loads here instead of hoisted.
-      CU32* qc = (CU32*)(qv + c);
-      asm volatile("" : "+s"(qc));
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        uint4 qq;
-        qq.x = qc[h * 64 + 0];
-        qq.y = qc[h * 64 + 1];
-        qq.z = qc[h * 64 + 2];
-        qq.w = qc[h * 64 + 3];
-        z[h] = dot2_bf16(kk.x, qq.x, z[h]);
-        z[h] = dot2_bf16(kk.y, qq.y, z[h]);
-        z[h] = dot2_bf16(kk.z, qq.z, z[h]);
-        z[h] = dot2_bf16(kk.w, qq.w, z[h]);
+    for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
+
+  for (int r0 = i0; r0 < i1; r0 += RR) {
+    if (r0 != i0) {
+      fetch_sel(r0);
+      fetch_pages(r0);
+    }
+    __syncthreads();  // the previous round's rows are no longer read
+    resolve_round(r0);
+    __syncthreads();  // rows (and, the first time, the query) visible
+    const int r1 = min(r0 + RR, i1);
+    uint4 kr[4][4];          // [token group][dim step]: A operands
+    uint2 vr[32];            // tokens 32*half + j, dims 4*c32 .. +3
+    uint32_t vmask = 0u;     // without BUF: bit j set = V row of token 32*half + j valid
+    // at < 0: no tile.
+    auto load_k = [&](int at) {
+      const int32_t none = at >= 0 ? 0 : -1;
+      const int32_t* rr = rowidx + (at >= 0 ? at - r0 : 0);
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int32_t rj = rr[16 * gi + c16] | none;
+        if constexpr (BUF) {
+          const uint32_t off = rj >= 0 ? (uint32_t)rj * (D * 2) + 16u * q4 : kOobOffset;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            kr[gi][db] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 64 * db, kStreamPolicy));
+        } else {
+          const uint16_t* src = kc + (int64_t)max(rj, 0) * D + 8 * q4;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            kr[gi][db] = __builtin_bit_cast(
+                uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + 32 * db)));
+        }
+      }
+    };
+    auto load_v = [&](int at) {
+      const int32_t none = at >= 0 ? 0 : -1;
+      const int32_t* rr = rowidx + (at >= 0 ? at - r0 : 0) + 32 * half;
+      uint32_t vm = 0u;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int32_t rj = rr[j] | none;
+        if constexpr (BUF) {
+          const uint32_t off = rj >= 0 ? (uint32_t)rj * (D * 2) + 8u * c32 : kOobOffset;
+          vr[j] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamPolicy));
+        } else {
+          vr[j] = __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(
+                                                vc + (int64_t)max(rj, 0) * D + 4 * c32)));
+          vm |= (rj >= 0 ? 1u : 0u) << j;
+        }
+      }
+      vmask = vm;
+    };
+    int it = r0 + 64 * wid;
+    if (it < r1) {
+      load_k(it);
+      load_v(it);
+      for (;;) {
+        const int nit = it + 64 * kWaves;
+        const bool has_next = nit < r1;
+        const int32_t* rows = rowidx + (it - r0);
+        const bool full = __all(rows[lane] >= 0);
+
+        uint4 qb[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) qb[db] = qs[c16][4 * db + q4];
+        f32x4_t z[4];
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+          z[gi] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            z[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, kr[gi][db]), __builtin_bit_cast(bf16x8_t, qb[db]),
+                z[gi], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(has_next ? nit : -1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Lane holds head c16 for tokens 16*gi + 4*q4 + e.
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v = z[gi][e] * g.attn_scale_log2;
+            if (!full && rows[16 * gi + 4 * q4 + e] < 0) v = -INFINITY;
+            z[gi][e] = v;
+            tmax = fmaxf(tmax, v);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m, tmax);
+        const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
+        m = mn;
+        float psum = 0.0f;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const float a = z[gi][2 * pr], c = z[gi][2 * pr + 1];
+            const uint32_t pa = (a == -INFINITY) ? 0u : bf16_rne(exp2f(a - mn));
+            const uint32_t pc = (c == -INFINITY) ? 0u : bf16_rne(exp2f(c - mn));
+            psum += bf_lo(pa) + bf_lo(pc);
+            if (c16 < G) PP[(8 * gi + 2 * q4 + pr) * G + c16] = pa | (pc << 16);
+          }
+        lp = fmaf(lp, alpha, psum);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+#pragma unroll
+          for (int d = 0; d < 4; ++d) o[h][d] *= ah;
+        }
+        wave_sync();
+
+#pragma unroll
+        for (int tp = 0; tp < 16; ++tp) {
+          uint2 va = vr[2 * tp], vb = vr[2 * tp + 1];
+          if constexpr (!BUF) {
+            const uint32_t ka = ((vmask >> (2 * tp)) & 1u) ? ~0u : 0u;
+            const uint32_t kb = ((vmask >> (2 * tp + 1)) & 1u) ? ~0u : 0u;
+            va.x &= ka;
+            va.y &= ka;
+            vb.x &= kb;
+            vb.y &= kb;
+          }
+          uint32_t vp[4];
+          vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
+          vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
+          vp[2] = __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u);
+          vp[3] = __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u);
+          const uint32_t* pr = PP + (16 * half + tp) * G;
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const uint32_t pw = pr[h];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o[h][d] = dot2_bf16(pw, vp[d], o[h][d]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_v(has_next ? nit : -1);
+        __builtin_amdgcn_sched_barrier(0);
+        wave_sync();
+        if (!has_next) break;
+        it = nit;
       }
     }
-
-    uint16_t* pp16 = reinterpret_cast<uint16_t*>(PP);
-    const int pslot = ((lane & 3) * 8 + (lane >> 3)) * G;  // this token's pair row
-    const int phalf = (lane >> 2) & 1;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float zz = (row >= 0) ? z[h] * g.attn_scale_log2 : -INFINITY;
-      const float mn = fmaxf(m[h], wave_max(zz));
-      const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2f(m[h] - mn);
-      const uint16_t pb = (zz == -INFINITY) ? (uint16_t)0 : bf16_rne(exp2f(zz - mn));
-      ls[h] = fmaf(ls[h], alpha, to_f32(pb));
-      m[h] = mn;
-#pragma unroll
-      for (int d = 0; d < 8; ++d) o[h][d] *= alpha;
-      pp16[(pslot + h) * 2 + phalf] = pb;
-    }
-    wave_sync();
-
-#pragma unroll
-    for (int mp = 0; mp < 8; ++mp) {
-      const uint4 va = vr[2 * mp], vb = vr[2 * mp + 1];
-      uint32_t vp[8];
-      vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
-      vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
-      vp[2] = __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u);
-      vp[3] = __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u);
-      vp[4] = __builtin_amdgcn_perm(vb.z, va.z, 0x05040100u);
-      vp[5] = __builtin_amdgcn_perm(vb.z, va.z, 0x07060302u);
-      vp[6] = __builtin_amdgcn_perm(vb.w, va.w, 0x05040100u);
-      vp[7] = __builtin_amdgcn_perm(vb.w, va.w, 0x07060302u);
-      const uint32_t* pr = PP + (grp * 8 + mp) * G;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t pw = pr[h];
-#pragma unroll
-        for (int d = 0; d < 8; ++d) o[h][d] = dot2_bf16(pw, vp[d], o[h][d]);
-      }
-    }
-    wave_sync();
-  }
   }
 
-  // Wave totals: l over all lanes, o over the four token groups.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float lt = wave_sum(ls[h]);
-    if (lane == 0) {
-      wm[wid][h] = m[h];
-      wl[wid][h] = lt;
-    }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      o[h][d] += __shfl_xor(o[h][d], 16, 64);
-      o[h][d] += __shfl_xor(o[h][d], 32, 64);
-    }
+  // Wave totals: l over the four lane rows of a head, o over the two token halves.
+  float lt = lp + __shfl_xor(lp, 16, 64);
+  lt += __shfl_xor(lt, 32, 64);
+  if (lane < G) {
+    wm[wid][lane] = m;
+    wl[wid][lane] = lt;
   }
-  // This wave's o -> its LDS region as fp32 [G][D] (group grp writes heads h%4 == grp).
-  float* wo = reinterpret_cast<float*>(Ks);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if ((h & 3) != grp) continue;
-    float4* dst = reinterpret_cast<float4*>(wo + h * D + cq * 8);
-    dst[0] = make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
-    dst[1] = make_float4(o[h][4], o[h][5], o[h][6], o[h][7]);
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[h][d] += __shfl_xor(o[h][d], 32, 64);
+  if (half == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      *reinterpret_cast<float4*>(&wo_all[wid][h * D + 4 * c32]) =
+          make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
   }
   __syncthreads();
 
   // Merge the 4 waves: thread -> EPT consecutive elements of one head.
   constexpr int EPT = (G * D >= 256) ? G * D / 256 : 1;
-  const int tid = threadIdx.x;
   const bool has_elem = tid * EPT < G * D;
   const int e0 = has_elem ? tid * EPT : 0, hh = e0 / D, d0 = e0 - hh * D;
   float M = -INFINITY;
@@ -927,13 +1069,13 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(
     const float mw = wm[w][hh];
     const float a = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
     Lw = fmaf(wl[w][hh], a, Lw);
-    const float* src = reinterpret_cast<const float*>(Ks_all[w]) + hh * D + d0;
+    const float* src = wo_all[w] + hh * D + d0;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) Ow[i] = fmaf(src[i], a, Ow[i]);
   }
 
   if (plan.n_splits == 1) {
-    if (!qp.ok || !has_elem) return;
+    if (!ok || !has_elem) return;
     const float inv = Lw > 0.0f ? 1.0f / Lw : 0.0f;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
@@ -951,7 +1093,7 @@ __global__ __launch_bounds__(256) void attn_bf16_d128_kernel(
   }
   if (has_elem && d0 == 0) {
     P[G * D + hh] = M;
-    P[G * D + G + hh] = Lw;
+    P[G * D + G + hh] = ok ? Lw : -1.0f;  // -1: the query lies outside the capacities
   }
 }
 
@@ -1174,10 +1316,20 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
   }
   dim3 grid(g.T * g.Hkv, plan.n_splits);
   if constexpr (sizeof(E) == 2 && D == 128) {
-    attn_bf16_d128_kernel<G><<<grid, 64 * kWaves, 0, st>>>(
-        g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-        static_cast<const uint16_t*>(v_cache), sel, n_blocks, static_cast<const uint16_t*>(gate),
-        static_cast<uint16_t*>(out), part);
+    const int64_t rows = g.page_table ? (int64_t)g.n_pages * g.Hkv * g.page_size
+                                      : (int64_t)g.B * g.Hkv * g.cap;
+    const int64_t bytes = rows * D * 2;
+    if (bytes < (int64_t)kOobOffset) {
+      attn_decode_kernel<G, true><<<grid, 64 * kWaves, 0, st>>>(
+          g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+          static_cast<const uint16_t*>(v_cache), sel, n_blocks,
+          static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out), part, (uint32_t)bytes);
+    } else {
+      attn_decode_kernel<G, false><<<grid, 64 * kWaves, 0, st>>>(
+          g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+          static_cast<const uint16_t*>(v_cache), sel, n_blocks,
+          static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out), part, 0u);
+    }
   } else {
     attn_split_kernel<E, G, D><<<grid, 64, 0, st>>>(
         g, plan, static_cast<const E*>(q), static_cast<const E*>(k_cache),
@@ -1185,7 +1337,7 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
         static_cast<E*>(out), part);
   }
   if (plan.n_splits > 1) {
-    attn_combine_kernel<E, G, D, kMaxSplits><<<g.T * g.Hkv, 256, 0, st>>>(
+    attn_combine_kernel<E, G, D><<<g.T * g.Hkv, 256, 0, st>>>(
         g, plan, part, static_cast<const E*>(gate), static_cast<E*>(out));
   }
   return hipGetLastError();

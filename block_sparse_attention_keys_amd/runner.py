@@ -33,12 +33,13 @@ class DeviceCase:
     n_layers independent copies of the caches can be made (the same values
     in distinct buffers), so that a benchmark can rotate over layers the way
     a model does and no step re-reads another step's data from cache memory.
+    page_offset places a paged cache's pages above that many unused pages.
     """
 
     def __init__(self, case: Case, device="cuda", n_layers: int = 1, extra_steps: int = 0,
                  layout: Optional[str] = None, attn_scale: float = 0.0,
                  idx_scale: float = 0.0, budget: Optional[int] = None,
-                 block_size: Optional[int] = None):
+                 block_size: Optional[int] = None, page_offset: int = 0):
         sp = case.spec
         self.case, self.spec, self.device = case, sp, torch.device(device)
         self.dt = torch.bfloat16 if sp.dtype == BF16 else torch.float32
@@ -59,7 +60,7 @@ class DeviceCase:
             ps = self.page_size
             self.cap = _round(cap_tok, ps)
             self.max_pages = self.cap // ps
-            if case.page_table is not None and extra_steps == 0 and layout is None:
+            if case.page_table is not None and extra_steps == 0 and layout is None and not page_offset:
                 pt = case.page_table.copy()
                 n_pages = case.n_pages
             else:  # build a permuted page table with room for the extra steps
@@ -73,6 +74,9 @@ class DeviceCase:
                     o += need[b]
             if pt.shape[1] < self.max_pages:
                 pt = np.concatenate([pt, np.full((B, self.max_pages - pt.shape[1]), -1, np.int32)], 1)
+            if page_offset:  # the sequences' pages at the top of a larger pool
+                pt = np.where(pt >= 0, pt + page_offset, pt).astype(np.int32)
+                n_pages += page_offset
             self.n_pages = int(n_pages)
             self.page_table_np = pt
             self.page_table = torch.from_numpy(pt).to(self.device)

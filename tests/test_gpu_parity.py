@@ -87,6 +87,23 @@ def test_long_decode_full_sampled_steps():
         assert np.array_equal(got[b, n // r - 2:n // r], ref)
 
 
+def test_paged_cache_over_4gib():
+    """K and V page pools of 4.3 GB each (rows past 2^24): the decode kernel
+    addresses them with 64-bit pointers instead of buffer offsets."""
+    case = workloads.make_case("ragged_paged_decode_128k_bf16", n_seqs=4, ctx_range=(2000, 9000))
+    _full(case, layout="paged", page_offset=131072)
+    torch.cuda.empty_cache()
+
+
+def test_dense_long_context_several_rounds():
+    """A dense layer over 140000 cached tokens: each split holds more list
+    positions than one round of row resolution."""
+    case = workloads.make_case("decode_32k_bf16", ctx=140000, steps=1)
+    dc = runner.DeviceCase(case, block_size=0)
+    res = run_calls(dc)
+    check_call(dc, SeqF32(case), res[0])
+
+
 # ----------------------------------------------------------------- the pages' case
 def test_pages_worked_count_released_config():
     """kv_len 3002, ratio 4, budget 2048: 512 of 750 blocks and 2050 keys
