@@ -259,7 +259,8 @@ qsa_status qsa_score_select(const qsa_params* params, const qsa_batch* batch,
   QSA_TRY(check_ws(pl, ws, ws_bytes));
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* scores = scores_opt ? scores_opt : reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
-  QSA_TRY(hip_status(qsa::launch_score(pl.geo, pl.elem, q_idx, w, pooled, scores, st),
+  QSA_TRY(hip_status(qsa::launch_score(pl.geo, pl.elem, q_idx, w, const_cast<float*>(pooled),
+                                       scores, st),
                      "score launch"));
   return hip_status(qsa::launch_select(pl.geo, scores, sel, n_blocks, st), "select launch");
 }
@@ -320,15 +321,27 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
   hipStream_t st = static_cast<hipStream_t>(stream);
   int32_t* sel = sel_opt ? sel_opt : reinterpret_cast<int32_t*>(ws_at(ws, pl.off_sel));
   int32_t* nblk = n_blocks_opt ? n_blocks_opt : reinterpret_cast<int32_t*>(ws_at(ws, pl.off_nblk));
-  QSA_TRY(hip_status(qsa::launch_append_pool(pl.geo, pl.elem, k_new, v_new,
-                                             qsa_layer ? k_idx_new : nullptr, k_cache, v_cache,
-                                             qsa_layer ? k_idx_cache : nullptr,
-                                             qsa_layer ? pooled : nullptr, st),
-                     "append/pool launch"));
+  if (qsa_layer && batch->max_q_len == 1) {
+    // Decode form: one launch appends, pools and scores.
+    float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
+    const qsa::AppendArgs ap = {k_new, v_new, k_idx_new, k_cache, v_cache, k_idx_cache};
+    QSA_TRY(hip_status(
+        qsa::launch_score_append(pl.geo, pl.elem, q_idx, w, pooled, scores, ap, st),
+        "append/score launch"));
+  } else {
+    QSA_TRY(hip_status(qsa::launch_append_pool(pl.geo, pl.elem, k_new, v_new,
+                                               qsa_layer ? k_idx_new : nullptr, k_cache, v_cache,
+                                               qsa_layer ? k_idx_cache : nullptr,
+                                               qsa_layer ? pooled : nullptr, st),
+                       "append/pool launch"));
+    if (qsa_layer) {
+      float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
+      QSA_TRY(hip_status(qsa::launch_score(pl.geo, pl.elem, q_idx, w, pooled, scores, st),
+                         "score launch"));
+    }
+  }
   if (qsa_layer) {
     float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
-    QSA_TRY(hip_status(qsa::launch_score(pl.geo, pl.elem, q_idx, w, pooled, scores, st),
-                       "score launch"));
     QSA_TRY(hip_status(qsa::launch_select(pl.geo, scores, sel, nblk, st), "select launch"));
   }
   float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));

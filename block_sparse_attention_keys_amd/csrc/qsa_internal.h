@@ -43,8 +43,20 @@ enum ElemType { kF32 = 0, kBF16 = 1 };
 hipError_t launch_append_pool(const Geo& g, int elem, const void* k_new, const void* v_new,
                               const void* kI_new, void* k_cache, void* v_cache, void* kI_cache,
                               float* pooled, hipStream_t st);
-hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w,
-                        const float* pooled, float* scores, hipStream_t st);
+hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w, float* pooled,
+                        float* scores, hipStream_t st);
+// Rows a decode-form score launch appends (at most one new token per sequence).
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const void* kI_new;
+  void* k_cache;
+  void* v_cache;
+  void* kI_cache;
+};
+hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const float* w,
+                               float* pooled, float* scores, const AppendArgs& ap,
+                               hipStream_t st);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
                          hipStream_t st);
 hipError_t launch_attend(const Geo& g, int elem, const AttnPlan& plan, const void* q,

@@ -84,6 +84,14 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Wave-local ordering of LDS traffic (within one wave; the waves of a workgroup
+// may be at different points).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Sequence of token t: the largest b with cu_q[b] <= t (cu_q ascending,
 // cu_q[0] = 0).  The wave reads 64 offsets at a time and counts them with a
 // ballot, so a batch of up to 64 sequences costs one memory round trip
@@ -207,18 +215,96 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
 // score: grid (T, ceil(nbcap/64)), one wave, one lane per candidate block.
 // The pooled cache is column-major per sequence, so for each dimension x the
 // wave reads 64 consecutive blocks (256 contiguous bytes).
-template <typename E, int HIM, int DI>
-__global__ __launch_bounds__(64) void score_kernel(Geo g, const E* __restrict__ qI,
-                                                   const float* __restrict__ w,
-                                                   const float* __restrict__ pooled,
-                                                   float* __restrict__ scores) {
+// APPEND: the decode form, where every sequence has at most one new token, so
+// no token of the call needs a row that another token appends.  The kernel
+// then also does the append: workgroup y = 0 of each token writes its K, V and
+// indexer-key rows, and the workgroup holding the block the token completes
+// pools that block (the new row from kI_new, the older rows from the cache,
+// summed in token order as in append_pool_kernel), scores it from LDS and
+// stores it in the pooled cache.
+template <typename E, int HIM, int DI, bool APPEND>
+__global__ __launch_bounds__(64) void score_kernel(
+    Geo g, const E* __restrict__ qI, const float* __restrict__ w, float* __restrict__ pooled,
+    float* __restrict__ scores, const E* __restrict__ k_new, const E* __restrict__ v_new,
+    const E* __restrict__ kI_new, E* __restrict__ k_cache, E* __restrict__ v_cache,
+    E* __restrict__ kI_cache) {
   __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
   __shared__ float wsh[HIM];
+  __shared__ float newpool[APPEND ? DI : 1];
   const int t = blockIdx.x, lane = threadIdx.x;
   const QueryPos qp = query_pos(g, t);
   const int nb = qp.ok ? ((qp.p + 1) >> g.log2r) : 0;
   const int j = blockIdx.y * 64 + lane;
   float* srow = scores + (int64_t)t * g.nbcap;
+  int jnew = -1;  // the block this token completes, pooled here
+  if constexpr (APPEND) {
+    constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
+    if (blockIdx.y == 0 && qp.ok) {
+      const int units = g.D / EPV, per = g.Hkv * units;
+      for (int u = lane; u < 2 * per; u += 64) {
+        const int which = u / per, rem = u - which * per;
+        const int kvh = rem / units, c = rem - kvh * units;
+        const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
+        if (dst < 0) continue;
+        const E* src = (which ? v_new : k_new) + ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV;
+        E* d = (which ? v_cache : k_cache) + dst + c * EPV;
+        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(src);
+      }
+      const int64_t drow = idx_row(g, qp.b, qp.p);
+      if (drow >= 0 && lane < DI / EPV)
+        *reinterpret_cast<uint4*>(kI_cache + drow + lane * EPV) =
+            *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * DI + lane * EPV);
+    }
+    if (qp.ok && ((qp.p + 1) & (g.r - 1)) == 0 && (int)blockIdx.y == (nb - 1) >> 6) {
+      // Rows of the block first (one page lookup per row, all lanes at once;
+      // -2 marks the new row), then chunks of rows staged in LDS with all
+      // loads in flight, then one lane per column adds them in token order.
+      constexpr int EPV = 16 / sizeof(E);
+      constexpr int UPR = DI / EPV;                        // 16-byte units per row
+      constexpr int RC = 16384 / (DI * (int)sizeof(E));    // rows per staged chunk
+      constexpr int CPT = DI >= 64 ? DI / 64 : 1;          // columns per lane
+      __shared__ int32_t prow[256];  // block_size <= 256
+      __shared__ __attribute__((aligned(16))) E stg[RC * DI];
+      jnew = nb - 1;
+      const int s0 = jnew << g.log2r;
+      for (int rr = lane; rr < g.r; rr += 64) {
+        const int sr = s0 + rr;
+        const int64_t row = sr == qp.p ? -2 : idx_row(g, qp.b, sr);
+        prow[rr] = row >= 0 ? (int32_t)(row / DI) : (int32_t)row;
+      }
+      wave_sync();
+      float acc[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) acc[c] = 0.0f;
+      for (int c0 = 0; c0 < g.r; c0 += RC) {
+        const int nrow = min(RC, g.r - c0);
+        for (int u = lane; u < nrow * UPR; u += 64) {
+          const int rr = u / UPR, cc = u - rr * UPR;
+          const int32_t pr = prow[c0 + rr];
+          const E* src = pr == -2 ? kI_new + (int64_t)t * DI : kI_cache + (int64_t)max(pr, 0) * DI;
+          uint4 v = *reinterpret_cast<const uint4*>(src + cc * EPV);
+          if (pr == -1) v = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(stg + rr * DI + cc * EPV) = v;
+        }
+        wave_sync();
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          const int x = lane + 64 * c;
+          if (x < DI)
+            for (int rr = 0; rr < nrow; ++rr) acc[c] = acc[c] + to_f32(stg[rr * DI + x]);
+        }
+        wave_sync();
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int x = lane + 64 * c;
+        if (x < DI) {
+          newpool[x] = acc[c] * g.inv_r;
+          pooled[((int64_t)qp.b * DI + x) * g.pooled_ld + jnew] = acc[c] * g.inv_r;
+        }
+      }
+    }
+  }
   float s = 0.0f;
   if ((int)blockIdx.y * 64 < nb) {
     const int HI = g.HI;
@@ -230,6 +316,7 @@ __global__ __launch_bounds__(64) void score_kernel(Geo g, const E* __restrict__ 
     __syncthreads();
     if (j < nb) {
       const float* pb = pooled + (int64_t)qp.b * DI * g.pooled_ld + j;
+      const bool fresh = APPEND && j == jnew;
       float acc[HIM];
 #pragma unroll
       for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
@@ -240,6 +327,10 @@ __global__ __launch_bounds__(64) void score_kernel(Geo g, const E* __restrict__ 
         float pk[16];
 #pragma unroll
         for (int xx = 0; xx < 16; ++xx) pk[xx] = pb[(int64_t)(x0 + xx) * g.pooled_ld];
+        if (fresh) {
+#pragma unroll
+          for (int xx = 0; xx < 16; ++xx) pk[xx] = newpool[x0 + xx];
+        }
 #pragma unroll
         for (int xx = 0; xx < 16; ++xx) {
           const float4* qrow = reinterpret_cast<const float4*>(qT + (x0 + xx) * HIM);
@@ -488,13 +579,6 @@ __device__ __forceinline__ int list_token(const Geo& g, const ListInfo& L,
   return L.tail0 + (i - L.nsel_tok);
 }
 
-// Wave-local ordering of LDS traffic (the waves of a workgroup run different
-// numbers of tiles, so the tile loop cannot use workgroup barriers).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // A split covers the 64-token tiles [tiles * s / S, tiles * (s + 1) / S) of the
 // longest list (S = n_splits): the same boundaries for every unit, so splits
@@ -779,7 +863,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   __shared__ __attribute__((aligned(16))) float wo_all[kWaves][G * D];
   __shared__ float wm[kWaves][G], wl[kWaves][G];
 
-  const int unit = blockIdx.x, split = blockIdx.y, tid = threadIdx.x;
+  // Splits run in reverse launch order: the splits that hold an extra tile
+  // (the last ones) are launched first, into the workgroup slots whose waves
+  // the hardware favours.
+  const int unit = blockIdx.x, split = plan.n_splits - 1 - blockIdx.y, tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c16 = lane & 15, q4 = lane >> 4;    // MFMA column, lane row group
   const int half = lane >> 5, c32 = lane & 31;  // PV: token half, 4-dim chunk
@@ -1364,26 +1451,32 @@ hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const voi
   }
 }
 
-template <typename E, int DI>
-void score_hd(const Geo& g, const void* qI, const float* w, const float* pooled,
-              float* scores, hipStream_t st) {
-  dim3 grid(g.T, (g.nbcap + 63) / 64);
+template <typename E, int DI, bool APPEND>
+void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
+              const AppendArgs& ap, hipStream_t st) {
+  dim3 grid(g.T, std::max(1, (g.nbcap + 63) / 64));
   const E* q = static_cast<const E*>(qI);
+  const E* kn = static_cast<const E*>(ap.k_new);
+  const E* vn = static_cast<const E*>(ap.v_new);
+  const E* in = static_cast<const E*>(ap.kI_new);
+  E* kc = static_cast<E*>(ap.k_cache);
+  E* vc = static_cast<E*>(ap.v_cache);
+  E* ic = static_cast<E*>(ap.kI_cache);
   if (g.HI <= 4) {
-    score_kernel<E, 4, DI><<<grid, 64, 0, st>>>(g, q, w, pooled, scores);
+    score_kernel<E, 4, DI, APPEND><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
   } else if (g.HI <= 8) {
-    score_kernel<E, 8, DI><<<grid, 64, 0, st>>>(g, q, w, pooled, scores);
+    score_kernel<E, 8, DI, APPEND><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
   } else {
-    score_kernel<E, 16, DI><<<grid, 64, 0, st>>>(g, q, w, pooled, scores);
+    score_kernel<E, 16, DI, APPEND><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
   }
 }
 
-template <typename E>
-hipError_t score_h(const Geo& g, const void* qI, const float* w, const float* pooled,
-                   float* scores, hipStream_t st) {
-  if (g.dI == 32) score_hd<E, 32>(g, qI, w, pooled, scores, st);
-  else if (g.dI == 64) score_hd<E, 64>(g, qI, w, pooled, scores, st);
-  else score_hd<E, 128>(g, qI, w, pooled, scores, st);
+template <typename E, bool APPEND>
+hipError_t score_h(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
+                   const AppendArgs& ap, hipStream_t st) {
+  if (g.dI == 32) score_hd<E, 32, APPEND>(g, qI, w, pooled, scores, ap, st);
+  else if (g.dI == 64) score_hd<E, 64, APPEND>(g, qI, w, pooled, scores, ap, st);
+  else score_hd<E, 128, APPEND>(g, qI, w, pooled, scores, ap, st);
   return hipGetLastError();
 }
 
@@ -1411,11 +1504,20 @@ hipError_t launch_append_pool(const Geo& g, int elem, const void* k_new, const v
   return hipGetLastError();
 }
 
-hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w,
-                        const float* pooled, float* scores, hipStream_t st) {
+hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w, float* pooled,
+                        float* scores, hipStream_t st) {
   if (g.T == 0 || g.nbcap == 0) return hipSuccess;
-  return elem == kBF16 ? score_h<uint16_t>(g, qI, w, pooled, scores, st)
-                       : score_h<float>(g, qI, w, pooled, scores, st);
+  const AppendArgs none = {};
+  return elem == kBF16 ? score_h<uint16_t, false>(g, qI, w, pooled, scores, none, st)
+                       : score_h<float, false>(g, qI, w, pooled, scores, none, st);
+}
+
+hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const float* w,
+                               float* pooled, float* scores, const AppendArgs& ap,
+                               hipStream_t st) {
+  if (g.T == 0) return hipSuccess;
+  return elem == kBF16 ? score_h<uint16_t, true>(g, qI, w, pooled, scores, ap, st)
+                       : score_h<float, true>(g, qI, w, pooled, scores, ap, st);
 }
 
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,

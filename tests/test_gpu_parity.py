@@ -74,6 +74,21 @@ def test_long_decode_reduced_crosses_block():
         assert np.array_equal(got[b, :ref.shape[0]], ref)
 
 
+def test_paged_decode_steps_cross_blocks():
+    """70 decode steps per sequence on a paged cache (one new token per
+    sequence: the launch that scores also appends and pools): every sequence
+    completes a block on the way, and the pooled cache equals from-scratch
+    pooling of the appended rows."""
+    case = workloads.make_case("ragged_paged_decode_128k_bf16", n_seqs=5, ctx_range=(30, 400),
+                               steps=70)
+    dc, _, _ = _full(case, layout="paged", keep={0, 1, 33, 69})
+    orc = oracle.load()
+    got = pooled_rows(dc)
+    for b in range(case.spec.n_seqs):
+        ref = orc.pool(case.kI[b], case.spec.block_size)
+        assert np.array_equal(got[b, :ref.shape[0]], ref)
+
+
 def test_long_decode_full_sampled_steps():
     case = workloads.make_case("long_decode_256k_bf16")
     keep = {0, 1, 64, 126, 127}
