@@ -37,7 +37,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr size_t kAlign = 256;
 constexpr int64_t kMfmaMinUnits = 512;  // (token, KV head) units that fill the chip without splits
-constexpr int kMaxK = 2048;
+constexpr int kMaxK = qsa::kPlanMaxK;
 
 struct Plan {
   qsa::Geo geo;
@@ -340,11 +340,22 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
                          "score launch"));
     }
   }
+  // Decode attention with few candidate blocks makes the selection itself
+  // (no separate select launch); otherwise select, then attend.
+  const bool fused = qsa_layer && !pl.attn.mfma && pl.elem == qsa::kBF16 && pl.geo.D == 128 &&
+                     pl.geo.nbcap <= qsa::kSelectInKernelMaxBlocks;
+  float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
+  if (fused) {
+    const qsa::InKernelSelect fs = {reinterpret_cast<const float*>(ws_at(ws, pl.off_scores)), sel,
+                                    nblk};
+    return hip_status(qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, nullptr,
+                                         nullptr, gate, out, part, st, fs),
+                      "attend launch");
+  }
   if (qsa_layer) {
     float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
     QSA_TRY(hip_status(qsa::launch_select(pl.geo, scores, sel, nblk, st), "select launch"));
   }
-  float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
   return hip_status(qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, sel, nblk,
                                        gate, out, part, st),
                     "attend launch");

@@ -33,6 +33,8 @@ struct AttnPlan {
   int32_t tiles;         // 64-token tiles of the longest selection list
 };
 constexpr int kPlanMaxSplits = 128;
+constexpr int kPlanMaxK = 2048;  // budget / block_size
+constexpr int kSelectInKernelMaxBlocks = 2048;  // candidate blocks the in-kernel selection holds
 
 // Waves per workgroup of the attention kernel chosen for this dtype / head dim.
 inline int attend_waves(int elem, int D) { return (elem == 1 && D == 128) ? 4 : 1; }
@@ -59,10 +61,17 @@ hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const flo
                                hipStream_t st);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
                          hipStream_t st);
+// In-kernel selection (decode attention): scores in, selections out (either
+// output may be null).  scores == null: the selection is read from sel.
+struct InKernelSelect {
+  const float* scores;
+  int32_t* sel_out;
+  int32_t* n_blocks_out;
+};
 hipError_t launch_attend(const Geo& g, int elem, const AttnPlan& plan, const void* q,
                          const void* k_cache, const void* v_cache, const int32_t* sel,
                          const int32_t* n_blocks, const void* gate, void* out, float* part,
-                         hipStream_t st);
+                         hipStream_t st, const InKernelSelect& fs = InKernelSelect{});
 
 // True when a kernel instantiation exists for G heads per KV head and dim D.
 bool attend_supported(int G, int D);

@@ -232,6 +232,16 @@ __global__ __launch_bounds__(64) void score_kernel(
   __shared__ float wsh[HIM];
   __shared__ float newpool[APPEND ? DI : 1];
   const int t = blockIdx.x, lane = threadIdx.x;
+  // The query and the head weights do not depend on the token's position:
+  // staged before the sequence search so the loads overlap.
+  {
+    const int HI = g.HI;
+    for (int e = lane; e < DI * HIM; e += 64) {
+      const int x = e / HIM, h = e - x * HIM;
+      qT[e] = h < HI ? to_f32(qI[((int64_t)t * HI + h) * DI + x]) : 0.0f;
+    }
+    if (lane < HIM) wsh[lane] = lane < HI ? w[(int64_t)t * HI + lane] : 0.0f;
+  }
   const QueryPos qp = query_pos(g, t);
   const int nb = qp.ok ? ((qp.p + 1) >> g.log2r) : 0;
   const int j = blockIdx.y * 64 + lane;
@@ -306,33 +316,29 @@ __global__ __launch_bounds__(64) void score_kernel(
     }
   }
   float s = 0.0f;
-  if ((int)blockIdx.y * 64 < nb) {
-    const int HI = g.HI;
-    for (int e = lane; e < DI * HIM; e += 64) {
-      const int x = e / HIM, h = e - x * HIM;
-      qT[e] = h < HI ? to_f32(qI[((int64_t)t * HI + h) * DI + x]) : 0.0f;
-    }
-    if (lane < HIM) wsh[lane] = lane < HI ? w[(int64_t)t * HI + lane] : 0.0f;
-    __syncthreads();
-    if (j < nb) {
+  __syncthreads();
+  if (j < nb) {
+    {
       const float* pb = pooled + (int64_t)qp.b * DI * g.pooled_ld + j;
       const bool fresh = APPEND && j == jnew;
+      const int HI = g.HI;
       float acc[HIM];
 #pragma unroll
       for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
-      // 16 dimensions per trip: their loads are all in flight, then each
+      // XC dimensions per trip: their loads are all in flight, then each
       // head's chain advances x in ascending order.
+      constexpr int XC = DI <= 32 ? 16 : 32;
 #pragma unroll 1
-      for (int x0 = 0; x0 < DI; x0 += 16) {
-        float pk[16];
+      for (int x0 = 0; x0 < DI; x0 += XC) {
+        float pk[XC];
 #pragma unroll
-        for (int xx = 0; xx < 16; ++xx) pk[xx] = pb[(int64_t)(x0 + xx) * g.pooled_ld];
+        for (int xx = 0; xx < XC; ++xx) pk[xx] = pb[(int64_t)(x0 + xx) * g.pooled_ld];
         if (fresh) {
 #pragma unroll
-          for (int xx = 0; xx < 16; ++xx) pk[xx] = newpool[x0 + xx];
+          for (int xx = 0; xx < XC; ++xx) pk[xx] = newpool[x0 + xx];
         }
 #pragma unroll
-        for (int xx = 0; xx < 16; ++xx) {
+        for (int xx = 0; xx < XC; ++xx) {
           const float4* qrow = reinterpret_cast<const float4*>(qT + (x0 + xx) * HIM);
 #pragma unroll
           for (int h4 = 0; h4 < HIM / 4; ++h4) {
@@ -393,6 +399,77 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
   return x - v;
 }
 
+// Top-k over keys held 8 per thread by a 256-thread workgroup: thread tid owns
+// the candidates [jb, jb + jn), jn <= 8, in index order (thread order = index
+// order, so the kept ids come out ascending).  The ids of the k largest keys,
+// ties to the lowest id, go to out (LDS or global).
+// 8-bit radix passes over the keys in registers (LDS histograms).
+__device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb, int jn, int k,
+                                                 int32_t* out) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_want;
+  __shared__ int sh[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t prefix = 0, mask = 0;
+  int want = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < jn && (kr[e] & mask) == prefix) atomicAdd(&hist[(kr[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wid == 0) {
+      // lane owns digits 255-4*lane .. 252-4*lane (descending)
+      int c[4], tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        c[i] = (int)hist[255 - 4 * lane - i];
+        tot += c[i];
+      }
+      int above = wave_excl_scan(tot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (above < want && above + c[i] >= want) {
+          s_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
+          s_want = want - above;
+        }
+        above += c[i];
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    want = s_want;
+    mask |= 255u << shift;
+  }
+  // Keep keys > prefix, and the first `want` keys == prefix in index order:
+  // one packed scan gives each thread both counts before it.
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < jn) {
+      n_gt += kr[e] > prefix ? 1 : 0;
+      n_eq += kr[e] == prefix ? 1 : 0;
+    }
+  }
+  int tot;
+  const int before = block_excl_scan((n_gt << 16) | n_eq, &tot, sh);
+  int pos = (before >> 16) + min(before & 0xffff, want);
+  int eqr = before & 0xffff;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < jn) {
+      const bool eq = kr[e] == prefix;
+      if (kr[e] > prefix || (eq && eqr < want)) {
+        if (pos < k) out[pos] = jb + e;
+        ++pos;
+      }
+      eqr += eq ? 1 : 0;
+    }
+  }
+}
+
 // select: one 256-thread workgroup per query.  Thread tid owns the contiguous
 // candidates [tid*per, tid*per + per); with per <= 8 (nb <= 2048) their keys
 // stay in registers across the passes.
@@ -410,11 +487,7 @@ __device__ __forceinline__ void select_impl(const Geo& g, const float* __restric
   const int per = (nb + 255) >> 8;
   const int jb = tid * per;
   const int jn = max(0, min(per, nb - jb));  // candidates this thread owns
-  uint32_t kr[8];
-  if (CACHED) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kr[e] = e < jn ? score_key(srow[jb + e]) : 0u;
-  }
+  uint32_t kr[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
   uint32_t prefix = 0, mask = 0;
   int want = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
@@ -517,9 +590,43 @@ __device__ __forceinline__ void select_impl(const Geo& g, const float* __restric
   (void)lane;
 }
 
+// select, up to 2048 candidate blocks: one 256-thread workgroup per query,
+// 8 keys per thread (block_radix_topk).  The scores are read before the query's
+// position is known (the row is -inf past its candidates), so that both
+// loads overlap.
+constexpr int kSelectMaxBlocks = 2048;
 __global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restrict__ scores,
                                                      int32_t* __restrict__ sel,
                                                      int32_t* __restrict__ n_blocks) {
+  const int t = blockIdx.x, tid = threadIdx.x, k = g.k;
+  const float* srow = scores + (int64_t)t * g.nbcap;
+  const int per = (g.nbcap + 255) >> 8;
+  const int jb = tid * per;
+  // Unconditional loads (clamped index, value masked after): conditional
+  // loads would each wait for the previous one.
+  uint32_t kr[8];
+  const int jlast = max(g.nbcap - 1, 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = srow[min(jb + e, jlast)];
+    kr[e] = (e < per && jb + e < g.nbcap) ? score_key(v) : 0u;
+  }
+  const QueryPos qp = query_pos(g, t);
+  const int nb = qp.ok ? min((qp.p + 1) >> g.log2r, g.nbcap) : 0;
+  int32_t* out = sel + (int64_t)t * k;
+  if (nb <= k) {  // every candidate is kept
+    for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
+  } else {
+    block_radix_topk(kr, jb, max(0, min(per, nb - jb)), k, out);
+  }
+  if (tid == 0) n_blocks[t] = min(k, nb);
+}
+
+// select, more candidate blocks: one 256-thread workgroup per query, 8-bit
+// radix passes over the scores in memory.
+__global__ __launch_bounds__(256) void select_large_kernel(Geo g, const float* __restrict__ scores,
+                                                           int32_t* __restrict__ sel,
+                                                           int32_t* __restrict__ n_blocks) {
   const int t = blockIdx.x, tid = threadIdx.x, k = g.k;
   const QueryPos qp = query_pos(g, t);
   // (min with the score row length only matters for inconsistent metadata)
@@ -530,9 +637,7 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restr
     if (tid == 0) n_blocks[t] = nb;
     return;
   }
-  const float* srow = scores + (int64_t)t * g.nbcap;
-  if (nb <= 2048) select_impl<true>(g, srow, nb, out);
-  else select_impl<false>(g, srow, nb, out);
+  select_impl<false>(g, scores + (int64_t)t * g.nbcap, nb, out);
   if (tid == 0) n_blocks[t] = k;
 }
 
@@ -847,12 +952,17 @@ constexpr int kStreamPolicy = 2;              // non-temporal: each K/V row is r
 // back zero, without memory traffic.  Otherwise they read row 0 and masked V
 // rows are zeroed in registers.  The 4 waves merge in LDS; a unit with several
 // splits writes one partial per split, merged by attn_combine_kernel.
-template <int G, bool BUF>
+// SEL: the top-k selection is made here from the scores (each workgroup of a
+// token makes the same selection; the workgroup of split 0, KV head 0 stores
+// it in sel / nblk when they are given), instead of being read from sel.
+template <int G, bool BUF, bool SEL>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     Geo g, AttnPlan plan, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
-    uint16_t* __restrict__ out, float* __restrict__ part, uint32_t kv_bytes) {
+    uint16_t* __restrict__ out, float* __restrict__ part, uint32_t kv_bytes,
+    const float* __restrict__ scores, int32_t* __restrict__ sel_out,
+    int32_t* __restrict__ nblk_out) {
   static_assert(G >= 1 && G <= 16 && 16 % G == 0, "heads per KV head must divide 16");
   constexpr int D = 128;
   constexpr int RR = 1024;       // list positions resolved per round
@@ -877,6 +987,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int sel_end = g.r > 0 ? (g.k << g.log2r) : 0;  // list positions that come from sel
   const int cap_blocks = g.r > 0 ? (g.cap >> g.log2r) : 0;
 
+  __shared__ int32_t sel_lds[SEL ? kPlanMaxK : 1];
+
+
   // Step 1 of the row resolution (independent loads).
   {
     const int hq = tid >> 4, ch = tid & 15;
@@ -884,16 +997,39 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
                                                           8 * ch)
                         : make_uint4(0u, 0u, 0u, 0u);
   }
-  const int nk_raw = g.r > 0 ? nblk[t] : 0;
+  int nk_raw = 0;
   int32_t sv[EPR], pg[EPR];
   auto fetch_sel = [&](int r0) {
 #pragma unroll
+    for (int j = 0; j < EPR; ++j) sv[j] = -1;
+    if (sel_end == 0) return;  // dense layer: no selection
+#pragma unroll
     for (int j = 0; j < EPR; ++j) {
       const int i = r0 + tid + 256 * j;
-      sv[j] = (i < sel_end) ? srow[i >> g.log2r] : -1;
+      // (clamped, unconditional loads: a conditional load waits for the last)
+      const int slot = min(i, sel_end - 1) >> g.log2r;
+      int32_t v;
+      if constexpr (SEL) v = sel_lds[max(slot, 0)];
+      else v = srow[max(slot, 0)];
+      sv[j] = (i < sel_end) ? v : -1;
     }
   };
-  fetch_sel(i0);
+  uint32_t kr_sel[8];  // SEL: the keys of this thread's candidates [jb_sel, jb_sel + per_sel)
+  const int per_sel = SEL ? (g.nbcap + 255) >> 8 : 0;
+  const int jb_sel = tid * per_sel;
+  if constexpr (SEL) {
+    // (unconditional loads at clamped indices; see select_kernel)
+    const float* srw = scores + (int64_t)t * g.nbcap;
+    const int jlast = max(g.nbcap - 1, 0);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float v = srw[min(jb_sel + e, jlast)];
+      kr_sel[e] = (e < per_sel && jb_sel + e < g.nbcap) ? score_key(v) : 0u;
+    }
+  } else {
+    if (g.r > 0) nk_raw = nblk[t];
+    fetch_sel(i0);
+  }
   const int b = seq_of(g.cu_q, g.B, t);
   // Token of position i if it lies in the selected part of the list, else -1.
   auto spec_token = [&](int i, int blk) -> int {
@@ -902,19 +1038,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
                                                          : -1;
   };
   auto fetch_pages = [&](int r0) {
+    if (g.page_table == nullptr) return;
 #pragma unroll
     for (int j = 0; j < EPR; ++j) {
       const int s = spec_token(r0 + tid + 256 * j, sv[j]);
-      pg[j] = (g.page_table != nullptr && s >= 0)
-                  ? g.page_table[(int64_t)b * g.max_pages + (s >> g.log2ps)]
-                  : -1;
+      const int v = g.page_table[(int64_t)b * g.max_pages + (max(s, 0) >> g.log2ps)];
+      pg[j] = s >= 0 ? v : -1;
     }
   };
   // Step 2: the position and the speculative pages.
   const int past = g.past_len[b], cu_b = g.cu_q[b];
-  fetch_pages(i0);
+  if constexpr (!SEL) fetch_pages(i0);
   const int p = past + (t - cu_b);
   const bool ok = p >= 0 && p < g.cap;
+  if constexpr (SEL) {
+    // The selection over the candidate blocks 0 .. nb-1 (all of them when
+    // there are at most k).
+    const int nb = ok ? min((p + 1) >> g.log2r, g.nbcap) : 0;
+    nk_raw = min(g.k, nb);
+    if (nb <= g.k) {
+      for (int i = tid; i < nb; i += 256) sel_lds[i] = i;
+    } else {
+      block_radix_topk(kr_sel, jb_sel, max(0, min(per_sel, nb - jb_sel)), g.k, sel_lds);
+    }
+    __syncthreads();
+    if (sel_out != nullptr && blockIdx.y == 0 && kvh == 0) {
+      for (int i = tid; i < g.k; i += 256) sel_out[(int64_t)t * g.k + i] = i < nk_raw ? sel_lds[i] : -1;
+      if (tid == 0 && nblk_out != nullptr) nblk_out[t] = nk_raw;
+    }
+    fetch_sel(i0);
+    fetch_pages(i0);
+  }
   ListInfo L = {0, 0, 0, 0};
   if (ok) {
     const int n = p + 1;
@@ -1391,7 +1545,11 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
 template <typename E, int G, int D>
 hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const void* k_cache,
                        const void* v_cache, const int32_t* sel, const int32_t* n_blocks,
-                       const void* gate, void* out, float* part, hipStream_t st) {
+                       const void* gate, void* out, float* part, const InKernelSelect& fs,
+                       hipStream_t st) {
+  const float* scores = fs.scores;
+  int32_t* sel_out = fs.sel_out;
+  int32_t* nblk_out = fs.n_blocks_out;
   if constexpr (sizeof(E) == 2 && D == 128) {
     if (plan.mfma) {
       attn_prefill_mfma_kernel<G><<<(g.T * g.Hkv + kWaves - 1) / kWaves, 64 * kWaves, 0, st>>>(
@@ -1406,16 +1564,21 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
     const int64_t rows = g.page_table ? (int64_t)g.n_pages * g.Hkv * g.page_size
                                       : (int64_t)g.B * g.Hkv * g.cap;
     const int64_t bytes = rows * D * 2;
-    if (bytes < (int64_t)kOobOffset) {
-      attn_decode_kernel<G, true><<<grid, 64 * kWaves, 0, st>>>(
-          g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-          static_cast<const uint16_t*>(v_cache), sel, n_blocks,
-          static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out), part, (uint32_t)bytes);
+    auto launch = [&](auto buf, auto fused) {
+      attn_decode_kernel<G, decltype(buf)::value, decltype(fused)::value>
+          <<<grid, 64 * kWaves, 0, st>>>(
+              g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+              static_cast<const uint16_t*>(v_cache), sel, n_blocks,
+              static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out), part,
+              decltype(buf)::value ? (uint32_t)bytes : 0u, scores, sel_out, nblk_out);
+    };
+    const bool buf = bytes < (int64_t)kOobOffset;
+    if (scores != nullptr) {
+      if (buf) launch(std::true_type{}, std::true_type{});
+      else launch(std::false_type{}, std::true_type{});
     } else {
-      attn_decode_kernel<G, false><<<grid, 64 * kWaves, 0, st>>>(
-          g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
-          static_cast<const uint16_t*>(v_cache), sel, n_blocks,
-          static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out), part, 0u);
+      if (buf) launch(std::true_type{}, std::false_type{});
+      else launch(std::false_type{}, std::false_type{});
     }
   } else {
     attn_split_kernel<E, G, D><<<grid, 64, 0, st>>>(
@@ -1433,21 +1596,21 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
 template <typename E, int G>
 hipError_t attend_d(const Geo& g, const AttnPlan& plan, const void* q, const void* kc,
                     const void* vc, const int32_t* sel, const int32_t* nb, const void* gate,
-                    void* out, float* part, hipStream_t st) {
-  if (g.D == 64) return attend_impl<E, G, 64>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
-  return attend_impl<E, G, 128>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
+                    void* out, float* part, const InKernelSelect& fs, hipStream_t st) {
+  if (g.D == 64) return attend_impl<E, G, 64>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
+  return attend_impl<E, G, 128>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
 }
 
 template <typename E>
 hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const void* kc,
                     const void* vc, const int32_t* sel, const int32_t* nb, const void* gate,
-                    void* out, float* part, hipStream_t st) {
+                    void* out, float* part, const InKernelSelect& fs, hipStream_t st) {
   switch (g.G) {
-    case 1: return attend_d<E, 1>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
-    case 2: return attend_d<E, 2>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
-    case 4: return attend_d<E, 4>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
-    case 8: return attend_d<E, 8>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
-    default: return attend_d<E, 16>(g, plan, q, kc, vc, sel, nb, gate, out, part, st);
+    case 1: return attend_d<E, 1>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
+    case 2: return attend_d<E, 2>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
+    case 4: return attend_d<E, 4>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
+    case 8: return attend_d<E, 8>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
+    default: return attend_d<E, 16>(g, plan, q, kc, vc, sel, nb, gate, out, part, fs, st);
   }
 }
 
@@ -1523,19 +1686,20 @@ hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const flo
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
                          hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  select_kernel<<<g.T, 256, 0, st>>>(g, scores, sel, n_blocks);
+  if (g.nbcap <= kSelectMaxBlocks) select_kernel<<<g.T, 256, 0, st>>>(g, scores, sel, n_blocks);
+  else select_large_kernel<<<g.T, 256, 0, st>>>(g, scores, sel, n_blocks);
   return hipGetLastError();
 }
 
 hipError_t launch_attend(const Geo& g, int elem, const AttnPlan& plan, const void* q,
                          const void* k_cache, const void* v_cache, const int32_t* sel,
                          const int32_t* n_blocks, const void* gate, void* out, float* part,
-                         hipStream_t st) {
+                         hipStream_t st, const InKernelSelect& fs) {
   if (g.T == 0) return hipSuccess;
   return elem == kBF16 ? attend_g<uint16_t>(g, plan, q, k_cache, v_cache, sel, n_blocks, gate,
-                                            out, part, st)
+                                            out, part, fs, st)
                        : attend_g<float>(g, plan, q, k_cache, v_cache, sel, n_blocks, gate, out,
-                                         part, st);
+                                         part, fs, st);
 }
 
 }  // namespace qsa

@@ -119,6 +119,34 @@ def test_dense_long_context_several_rounds():
     check_call(dc, SeqF32(case), res[0])
 
 
+def test_selection_ties_all_scores_equal():
+    """Zero indexer queries: every candidate block scores 0, so the selection
+    is the tie rule alone (the lowest block ids)."""
+    case = workloads.make_case("decode_32k_bf16", ctx=9000, steps=2)
+    for b in range(case.spec.n_seqs):
+        case.qI[b][:] = 0
+    _full(case)
+
+
+def test_selection_ties_at_the_boundary():
+    """Indexer keys with a negative first dimension except in five blocks,
+    and queries that read only that dimension: five blocks share one positive
+    score and all others score 0, so the k-th largest score is a tie broken
+    by block id."""
+    case = workloads.make_case("decode_32k_bf16", ctx=9000, steps=2)
+    r = case.spec.block_size
+    for b in range(case.spec.n_seqs):
+        kI = workloads.as_f32(case.kI[b]).copy()
+        kI[:, 0] = -1.0
+        for blk in (3, 10, 50, 77, 100):
+            kI[blk * r:(blk + 1) * r, 0] = 1.0
+        case.kI[b] = workloads.bf16_bits(kI)
+        qI = np.zeros(case.qI[b].shape, np.float32)
+        qI[..., 0] = 1.0
+        case.qI[b] = workloads.bf16_bits(qI)
+    _full(case)
+
+
 # ----------------------------------------------------------------- the pages' case
 def test_pages_worked_count_released_config():
     """kv_len 3002, ratio 4, budget 2048: 512 of 750 blocks and 2050 keys
