@@ -122,6 +122,7 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   g.k = k;
   g.B = b.n_seqs;
   g.T = b.n_tokens;
+  g.one_q = (b.n_tokens == b.n_seqs && b.max_q_len == 1) ? 1 : 0;
   g.cap = b.kv_capacity;
   g.page_size = b.page_size;
   g.log2ps = b.page_size ? ilog2(b.page_size) : 0;

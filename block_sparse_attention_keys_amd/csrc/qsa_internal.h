@@ -13,6 +13,7 @@ struct Geo {
   int32_t HI, dI;              // indexer heads and dim
   int32_t r, log2r, k;         // block size (0 = dense), log2, blocks kept
   int32_t B, T;                // sequences, new tokens
+  int32_t one_q;               // 1: every sequence has exactly one new token (t = b)
   int32_t cap;                 // rows per sequence
   int32_t page_size, log2ps;   // 0 = contiguous
   int32_t max_pages, n_pages;

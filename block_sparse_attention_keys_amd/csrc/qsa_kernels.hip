@@ -59,8 +59,27 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// v combined with the value of lane l ^ 16 (or l ^ 32): the gfx950 row swaps
+// hand each lane both values of its pair (in some order), on the VALU.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-wide reductions: four DPP steps inside each row of 16 lanes (xor 1,
-// xor 2, half-row mirror, row mirror), then two cross-row exchanges.
+// xor 2, half-row mirror, row mirror), then the two cross-row swaps.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -70,18 +89,14 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]
   v = fmaxf(v, dpp<0x141>(v));  // row_half_mirror
   v = fmaxf(v, dpp<0x140>(v));  // row_mirror
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  return max_xor32(max_xor16(v));
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0xB1>(v);
   v += dpp<0x4E>(v);
   v += dpp<0x141>(v);
   v += dpp<0x140>(v);
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  return sum_xor32(sum_xor16(v));
 }
 
 // Wave-local ordering of LDS traffic (within one wave; the waves of a workgroup
@@ -113,10 +128,17 @@ struct QueryPos {
   int b, p;
   bool ok;
 };
+// With one new token per sequence, token t is sequence t's token and cu_q[t]
+// = t: one load instead of three dependent ones.
 __device__ __forceinline__ QueryPos query_pos(const Geo& g, int t) {
   QueryPos q;
-  q.b = seq_of(g.cu_q, g.B, t);
-  q.p = g.past_len[q.b] + (t - g.cu_q[q.b]);
+  if (g.one_q) {
+    q.b = t;
+    q.p = g.past_len[t];
+  } else {
+    q.b = seq_of(g.cu_q, g.B, t);
+    q.p = g.past_len[q.b] + (t - g.cu_q[q.b]);
+  }
   q.ok = q.p >= 0 && q.p < g.cap;
   return q;
 }
@@ -365,14 +387,26 @@ __global__ __launch_bounds__(64) void score_kernel(
 
 // ---------------------------------------------------------------------------
 // Exclusive prefix sum over a 256-thread workgroup (4 waves).
+// Inclusive prefix sum over one wave on DPP: shifts by 1, 2, 4, 8 lanes inside
+// each 16-lane row (zero shifted in), then the row totals are carried by the
+// lane-15 and lane-31 broadcasts.  No LDS round trips.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Exclusive prefix sum over one wave.
+__device__ __forceinline__ int wave_excl_scan(int v) { return wave_incl_scan(v) - v; }
+
+// Exclusive prefix sum over a 256-thread workgroup (sh: 4 ints of LDS).
 __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63) sh[wid] = x;
   __syncthreads();
   int off = 0, tot = 0;
@@ -387,18 +421,6 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
   return off + x - v;
 }
 
-// Exclusive prefix sum over one wave.
-__device__ __forceinline__ int wave_excl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x - v;
-}
-
 // Top-k over keys held 8 per thread by a 256-thread workgroup: thread tid owns
 // the candidates [jb, jb + jn), jn <= 8, in index order (thread order = index
 // order, so the kept ids come out ascending).  The ids of the k largest keys,
@@ -406,29 +428,30 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
 // 8-bit radix passes over the keys in registers (LDS histograms).
 __device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb, int jn, int k,
                                                  int32_t* out) {
-  __shared__ uint32_t hist[256];
+  // Two histograms: while wave 0 scans one, the other is cleared for the next
+  // pass, so a pass costs two barriers.
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][256];
   __shared__ uint32_t s_prefix;
   __shared__ int s_want;
   __shared__ int sh[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t prefix = 0, mask = 0;
   int want = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
+  hist[0][tid] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    uint32_t* hc = hist[pass & 1];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (e < jn && (kr[e] & mask) == prefix) atomicAdd(&hist[(kr[e] >> shift) & 255u], 1u);
+      if (e < jn && (kr[e] & mask) == prefix) atomicAdd(&hc[(kr[e] >> shift) & 255u], 1u);
     __syncthreads();
     if (wid == 0) {
       // lane owns digits 255-4*lane .. 252-4*lane (descending)
-      int c[4], tot = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = (int)hist[255 - 4 * lane - i];
-        tot += c[i];
-      }
-      int above = wave_excl_scan(tot);
+      const uint4 h4 = *reinterpret_cast<const uint4*>(&hc[252 - 4 * lane]);
+      const int c[4] = {(int)h4.w, (int)h4.z, (int)h4.y, (int)h4.x};
+      int above = wave_excl_scan(c[0] + c[1] + c[2] + c[3]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (above < want && above + c[i] >= want) {
@@ -438,6 +461,7 @@ __device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb
         above += c[i];
       }
     }
+    if (pass < 3) hist[(pass + 1) & 1][tid] = 0;
     __syncthreads();
     prefix = s_prefix;
     want = s_want;
@@ -1030,7 +1054,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     if (g.r > 0) nk_raw = nblk[t];
     fetch_sel(i0);
   }
-  const int b = seq_of(g.cu_q, g.B, t);
+  const int b = g.one_q ? t : seq_of(g.cu_q, g.B, t);
   // Token of position i if it lies in the selected part of the list, else -1.
   auto spec_token = [&](int i, int blk) -> int {
     if (g.r == 0) return i < g.cap ? i : -1;
@@ -1047,7 +1071,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     }
   };
   // Step 2: the position and the speculative pages.
-  const int past = g.past_len[b], cu_b = g.cu_q[b];
+  const int past = g.past_len[b], cu_b = g.one_q ? t : g.cu_q[b];
   if constexpr (!SEL) fetch_pages(i0);
   const int p = past + (t - cu_b);
   const bool ok = p >= 0 && p < g.cap;
@@ -1217,8 +1241,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
             z[gi][e] = v;
             tmax = fmaxf(tmax, v);
           }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        tmax = max_xor32(max_xor16(tmax));
         const float mn = fmaxf(m, tmax);
         const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
         m = mn;
@@ -1277,8 +1300,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 
   // Wave totals: l over the four lane rows of a head, o over the two token halves.
-  float lt = lp + __shfl_xor(lp, 16, 64);
-  lt += __shfl_xor(lt, 32, 64);
+  const float lt = sum_xor32(sum_xor16(lp));
   if (lane < G) {
     wm[wid][lane] = m;
     wl[wid][lane] = lt;
@@ -1286,7 +1308,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int d = 0; d < 4; ++d) o[h][d] += __shfl_xor(o[h][d], 32, 64);
+    for (int d = 0; d < 4; ++d) o[h][d] = sum_xor32(o[h][d]);
   if (half == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
