@@ -59,6 +59,15 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Buffer resource over [base, base + bytes): loads at or past the end return
+// zeros (raw buffer, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+constexpr uint32_t kOobOffset = 0xFFFFF000u;  // past the end of every buffer that uses it
+constexpr int kStreamPolicy = 2;              // non-temporal: each K/V row is read once
+
 // v combined with the value of lane l ^ 16 (or l ^ 32): the gfx950 row swaps
 // hand each lane both values of its pair (in some order), on the VALU.
 __device__ __forceinline__ float max_xor16(float v) {
@@ -236,24 +245,32 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
 // ---------------------------------------------------------------------------
 // score: grid (T, ceil(nbcap/64)), one wave, one lane per candidate block.
 // The pooled cache is column-major per sequence, so for each dimension x the
-// wave reads 64 consecutive blocks (256 contiguous bytes).
-// APPEND: the decode form, where every sequence has at most one new token, so
-// no token of the call needs a row that another token appends.  The kernel
+// wave reads 64 consecutive blocks (256 contiguous bytes); each lane holds all
+// d_I values of its block's pooled key in registers, loaded together.
+// MODE 0: scoring only (the pooled cache is complete).
+// MODE 1, 2: the decode form, where every sequence has at most one new token,
+// so no token of the call needs a row that another token appends.  The kernel
 // then also does the append: workgroup y = 0 of each token writes its K, V and
-// indexer-key rows, and the workgroup holding the block the token completes
-// pools that block (the new row from kI_new, the older rows from the cache,
-// summed in token order as in append_pool_kernel), scores it from LDS and
-// stores it in the pooled cache.
-template <typename E, int HIM, int DI, bool APPEND>
+// indexer-key rows (read before the position is known), and the workgroup
+// holding the block the token completes pools that block (the new row from
+// kI_new, the older rows from the cache, summed in token order as in
+// append_pool_kernel), scores it from LDS and stores it in the pooled cache.
+// MODE 2: every sequence has exactly one new token (token t is sequence t's),
+// so the pooled keys are read before the position is known as well: one
+// memory round trip for the workgroups that neither append nor pool.
+template <typename E, int HIM, int DI, int MODE>
 __global__ __launch_bounds__(64) void score_kernel(
     Geo g, const E* __restrict__ qI, const float* __restrict__ w, float* __restrict__ pooled,
     float* __restrict__ scores, const E* __restrict__ k_new, const E* __restrict__ v_new,
     const E* __restrict__ kI_new, E* __restrict__ k_cache, E* __restrict__ v_cache,
     E* __restrict__ kI_cache) {
+  constexpr bool APPEND = MODE != 0, ONEQ = MODE == 2;
+  constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
   __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
   __shared__ float wsh[HIM];
   __shared__ float newpool[APPEND ? DI : 1];
   const int t = blockIdx.x, lane = threadIdx.x;
+  const int j = blockIdx.y * 64 + lane;
   // The query and the head weights do not depend on the token's position:
   // staged before the sequence search so the loads overlap.
   {
@@ -264,34 +281,69 @@ __global__ __launch_bounds__(64) void score_kernel(
     }
     if (lane < HIM) wsh[lane] = lane < HI ? w[(int64_t)t * HI + lane] : 0.0f;
   }
+  // Decode form, workgroup 0: this token's new rows, 16 bytes per lane and
+  // load (the first 4 per lane held across the position lookup).
+  const bool appender = APPEND && blockIdx.y == 0;
+  const int kv_units = APPEND ? 2 * g.Hkv * (g.D / EPV) : 0;
+  uint4 kvv[4], kiv = make_uint4(0u, 0u, 0u, 0u);
+  if (appender) {
+    const int per = kv_units >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = min(lane + 64 * i, kv_units - 1);
+      const int which = u >= per ? 1 : 0;
+      kvv[i] = *reinterpret_cast<const uint4*>((which ? v_new : k_new) +
+                                               (int64_t)t * g.Hkv * g.D + (u - which * per) * EPV);
+    }
+    kiv = *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * DI + min(lane, DI / EPV - 1) * EPV);
+  }
+  // The lane's pooled key (unconditional loads at a clamped column).
+  // (Buffer loads: one column offset per lane, the row offset in a scalar.)
+  float pk[DI];
+  auto load_keys = [&](int b) {
+    const __amdgpu_buffer_rsrc_t rs =
+        buffer_rsrc(pooled + (int64_t)b * DI * g.pooled_ld, (uint32_t)(DI * g.pooled_ld * 4));
+    const uint32_t col = (uint32_t)min(j, g.pooled_ld - 1) * 4u;
+#pragma unroll
+    for (int x = 0; x < DI; ++x)
+      pk[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            rs, col, (uint32_t)(x * g.pooled_ld * 4), 0));
+  };
+  if constexpr (ONEQ) load_keys(t);
   const QueryPos qp = query_pos(g, t);
   const int nb = qp.ok ? ((qp.p + 1) >> g.log2r) : 0;
-  const int j = blockIdx.y * 64 + lane;
+  if constexpr (!ONEQ) {
+    if ((int)blockIdx.y * 64 < nb) load_keys(qp.b);
+  }
   float* srow = scores + (int64_t)t * g.nbcap;
   int jnew = -1;  // the block this token completes, pooled here
   if constexpr (APPEND) {
-    constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
-    if (blockIdx.y == 0 && qp.ok) {
-      const int units = g.D / EPV, per = g.Hkv * units;
-      for (int u = lane; u < 2 * per; u += 64) {
-        const int which = u / per, rem = u - which * per;
+    if (appender && qp.ok) {
+      const int per = kv_units >> 1, units = g.D / EPV;
+      for (int u = lane; u < kv_units; u += 64) {
+        const int which = u >= per ? 1 : 0, rem = u - which * per;
         const int kvh = rem / units, c = rem - kvh * units;
         const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
         if (dst < 0) continue;
-        const E* src = (which ? v_new : k_new) + ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV;
-        E* d = (which ? v_cache : k_cache) + dst + c * EPV;
-        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(src);
+        uint4 v;
+        const int i = (u - lane) >> 6;
+        if (i < 4) {
+          v = kvv[0];
+#pragma unroll
+          for (int ii = 1; ii < 4; ++ii) v = (i == ii) ? kvv[ii] : v;
+        } else {
+          v = *reinterpret_cast<const uint4*>((which ? v_new : k_new) +
+                                              ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV);
+        }
+        *reinterpret_cast<uint4*>((which ? v_cache : k_cache) + dst + c * EPV) = v;
       }
       const int64_t drow = idx_row(g, qp.b, qp.p);
-      if (drow >= 0 && lane < DI / EPV)
-        *reinterpret_cast<uint4*>(kI_cache + drow + lane * EPV) =
-            *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * DI + lane * EPV);
+      if (drow >= 0 && lane < DI / EPV) *reinterpret_cast<uint4*>(kI_cache + drow + lane * EPV) = kiv;
     }
     if (qp.ok && ((qp.p + 1) & (g.r - 1)) == 0 && (int)blockIdx.y == (nb - 1) >> 6) {
       // Rows of the block first (one page lookup per row, all lanes at once;
       // -2 marks the new row), then chunks of rows staged in LDS with all
       // loads in flight, then one lane per column adds them in token order.
-      constexpr int EPV = 16 / sizeof(E);
       constexpr int UPR = DI / EPV;                        // 16-byte units per row
       constexpr int RC = 16384 / (DI * (int)sizeof(E));    // rows per staged chunk
       constexpr int CPT = DI >= 64 ? DI / 64 : 1;          // columns per lane
@@ -337,48 +389,52 @@ __global__ __launch_bounds__(64) void score_kernel(
       }
     }
   }
-  float s = 0.0f;
   __syncthreads();
-  if (j < nb) {
-    {
-      const float* pb = pooled + (int64_t)qp.b * DI * g.pooled_ld + j;
-      const bool fresh = APPEND && j == jnew;
-      const int HI = g.HI;
-      float acc[HIM];
+  float s = 0.0f;
+  if ((int)blockIdx.y * 64 < nb) {
+    if (APPEND && j == jnew) {
 #pragma unroll
-      for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
-      // XC dimensions per trip: their loads are all in flight, then each
-      // head's chain advances x in ascending order.
-      constexpr int XC = DI <= 32 ? 16 : 32;
+      for (int x = 0; x < DI; ++x) pk[x] = newpool[x];
+    }
+    float acc[HIM];
+#pragma unroll
+    for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
+    // Chunks of XC dimensions in a loop that is not unrolled (so the query
+    // reads of one chunk are not hoisted into registers ahead of the others),
+    // the chunk's keys picked out of the registers by selects; each head's
+    // chain advances x in ascending order.
+    constexpr int XC = DI <= 32 ? 16 : 32;
+    constexpr int NCH = DI / XC;
 #pragma unroll 1
-      for (int x0 = 0; x0 < DI; x0 += XC) {
-        float pk[XC];
+    for (int c = 0; c < NCH; ++c) {
+      float pc[XC];
 #pragma unroll
-        for (int xx = 0; xx < XC; ++xx) pk[xx] = pb[(int64_t)(x0 + xx) * g.pooled_ld];
-        if (fresh) {
+      for (int xx = 0; xx < XC; ++xx) {
+        float v = pk[xx];
 #pragma unroll
-          for (int xx = 0; xx < XC; ++xx) pk[xx] = newpool[x0 + xx];
-        }
-#pragma unroll
-        for (int xx = 0; xx < XC; ++xx) {
-          const float4* qrow = reinterpret_cast<const float4*>(qT + (x0 + xx) * HIM);
-#pragma unroll
-          for (int h4 = 0; h4 < HIM / 4; ++h4) {
-            const float4 qv = qrow[h4];
-            acc[4 * h4 + 0] = fmaf(qv.x, pk[xx], acc[4 * h4 + 0]);
-            acc[4 * h4 + 1] = fmaf(qv.y, pk[xx], acc[4 * h4 + 1]);
-            acc[4 * h4 + 2] = fmaf(qv.z, pk[xx], acc[4 * h4 + 2]);
-            acc[4 * h4 + 3] = fmaf(qv.w, pk[xx], acc[4 * h4 + 3]);
-          }
-        }
+        for (int cc = 1; cc < NCH; ++cc) v = (c == cc) ? pk[cc * XC + xx] : v;
+        pc[xx] = v;
       }
 #pragma unroll
-      for (int h = 0; h < HIM; ++h) {
-        if (h < HI) {
-          float a = g.idx_scale * acc[h];
-          a = (a > 0.0f) ? a : 0.0f;
-          s = fmaf(wsh[h], a, s);
+      for (int xx = 0; xx < XC; ++xx) {
+        const float4* qrow = reinterpret_cast<const float4*>(qT + (c * XC + xx) * HIM);
+#pragma unroll
+        for (int h4 = 0; h4 < HIM / 4; ++h4) {
+          const float4 qv = qrow[h4];
+          acc[4 * h4 + 0] = fmaf(qv.x, pc[xx], acc[4 * h4 + 0]);
+          acc[4 * h4 + 1] = fmaf(qv.y, pc[xx], acc[4 * h4 + 1]);
+          acc[4 * h4 + 2] = fmaf(qv.z, pc[xx], acc[4 * h4 + 2]);
+          acc[4 * h4 + 3] = fmaf(qv.w, pc[xx], acc[4 * h4 + 3]);
         }
+      }
+    }
+    const int HI = g.HI;
+#pragma unroll
+    for (int h = 0; h < HIM; ++h) {
+      if (h < HI) {
+        float a = g.idx_scale * acc[h];
+        a = (a > 0.0f) ? a : 0.0f;
+        s = fmaf(wsh[h], a, s);
       }
     }
   }
@@ -386,7 +442,6 @@ __global__ __launch_bounds__(64) void score_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Exclusive prefix sum over a 256-thread workgroup (4 waves).
 // Inclusive prefix sum over one wave on DPP: shifts by 1, 2, 4, 8 lanes inside
 // each 16-lane row (zero shifted in), then the row totals are carried by the
 // lane-15 and lane-31 broadcasts.  No LDS round trips.
@@ -939,14 +994,6 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
   }
 }
 
-// Buffer resource over [base, base + bytes): loads at or past the end return
-// zeros (raw buffer, no stride).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-constexpr uint32_t kOobOffset = 0xFFFFF000u;  // past the end of every buffer that uses it
-constexpr int kStreamPolicy = 2;              // non-temporal: each K/V row is read once
 
 // bf16, D = 128 decode kernel.  A workgroup of 4 waves owns one split of one
 // (token, KV head) unit; its waves take the split's 64-token tiles in turn.
@@ -967,9 +1014,9 @@ constexpr int kStreamPolicy = 2;              // non-temporal: each K/V row is r
 //   PV on the vector ALU: a lane holds 4 dims of 32 tokens of V (8-byte
 //     chunks, two full rows per load instruction) and accumulates bf16 dot2
 //     over token pairs, the p pairs read from LDS as broadcasts.
-// The next tile's K is loaded right after this tile's QK and its V right after
+// The next tile's K is requested after this tile's softmax and its V after
 // this tile's PV, so each wave keeps a tile of loads in flight while it
-// computes.  The loads are unconditional (a wave's last look-ahead reads
+// computes (requesting K right after QK, with more in flight, streams slower).  The loads are unconditional (a wave's last look-ahead reads
 // nothing useful): conditional loads would keep two copies of the tile
 // registers alive.  With BUF (caches under 4 GiB) K and V go through buffer
 // resources: masked rows and the last look-ahead read past the end and come
@@ -1226,9 +1273,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
                 __builtin_bit_cast(bf16x8_t, kr[gi][db]), __builtin_bit_cast(bf16x8_t, qb[db]),
                 z[gi], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        load_k(has_next ? nit : -1);
-        __builtin_amdgcn_sched_barrier(0);
 
         // Lane holds head c16 for tokens 16*gi + 4*q4 + e.
         float tmax = -INFINITY;
@@ -1265,6 +1309,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         }
         wave_sync();
 
+        // The next tile's K is requested only now, after the softmax: fewer
+        // requests in flight at once stream faster on this memory system.
+        __builtin_amdgcn_sched_barrier(0);
+        load_k(has_next ? nit : -1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tp = 0; tp < 16; ++tp) {
           uint2 va = vr[2 * tp], vb = vr[2 * tp + 1];
@@ -1636,7 +1685,7 @@ hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const voi
   }
 }
 
-template <typename E, int DI, bool APPEND>
+template <typename E, int DI, int MODE>
 void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
               const AppendArgs& ap, hipStream_t st) {
   dim3 grid(g.T, std::max(1, (g.nbcap + 63) / 64));
@@ -1648,20 +1697,20 @@ void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float
   E* vc = static_cast<E*>(ap.v_cache);
   E* ic = static_cast<E*>(ap.kI_cache);
   if (g.HI <= 4) {
-    score_kernel<E, 4, DI, APPEND><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
+    score_kernel<E, 4, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
   } else if (g.HI <= 8) {
-    score_kernel<E, 8, DI, APPEND><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
+    score_kernel<E, 8, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
   } else {
-    score_kernel<E, 16, DI, APPEND><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
+    score_kernel<E, 16, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
   }
 }
 
-template <typename E, bool APPEND>
+template <typename E, int MODE>
 hipError_t score_h(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
                    const AppendArgs& ap, hipStream_t st) {
-  if (g.dI == 32) score_hd<E, 32, APPEND>(g, qI, w, pooled, scores, ap, st);
-  else if (g.dI == 64) score_hd<E, 64, APPEND>(g, qI, w, pooled, scores, ap, st);
-  else score_hd<E, 128, APPEND>(g, qI, w, pooled, scores, ap, st);
+  if (g.dI == 32) score_hd<E, 32, MODE>(g, qI, w, pooled, scores, ap, st);
+  else if (g.dI == 64) score_hd<E, 64, MODE>(g, qI, w, pooled, scores, ap, st);
+  else score_hd<E, 128, MODE>(g, qI, w, pooled, scores, ap, st);
   return hipGetLastError();
 }
 
@@ -1693,16 +1742,19 @@ hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w, 
                         float* scores, hipStream_t st) {
   if (g.T == 0 || g.nbcap == 0) return hipSuccess;
   const AppendArgs none = {};
-  return elem == kBF16 ? score_h<uint16_t, false>(g, qI, w, pooled, scores, none, st)
-                       : score_h<float, false>(g, qI, w, pooled, scores, none, st);
+  return elem == kBF16 ? score_h<uint16_t, 0>(g, qI, w, pooled, scores, none, st)
+                       : score_h<float, 0>(g, qI, w, pooled, scores, none, st);
 }
 
 hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const float* w,
                                float* pooled, float* scores, const AppendArgs& ap,
                                hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  return elem == kBF16 ? score_h<uint16_t, true>(g, qI, w, pooled, scores, ap, st)
-                       : score_h<float, true>(g, qI, w, pooled, scores, ap, st);
+  if (g.one_q)
+    return elem == kBF16 ? score_h<uint16_t, 2>(g, qI, w, pooled, scores, ap, st)
+                         : score_h<float, 2>(g, qI, w, pooled, scores, ap, st);
+  return elem == kBF16 ? score_h<uint16_t, 1>(g, qI, w, pooled, scores, ap, st)
+                       : score_h<float, 1>(g, qI, w, pooled, scores, ap, st);
 }
 
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
