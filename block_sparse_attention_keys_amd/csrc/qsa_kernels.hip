@@ -243,21 +243,44 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// score: grid (T, ceil(nbcap/64)), one wave, one lane per candidate block.
-// The pooled cache is column-major per sequence, so for each dimension x the
-// wave reads 64 consecutive blocks (256 contiguous bytes); each lane holds all
-// d_I values of its block's pooled key in registers, loaded together.
+// score: one wave per workgroup; grid (T, ceil(nbcap/64)) scoring workgroups,
+// one lane per candidate block.  The pooled cache is column-major per
+// sequence, so for each dimension x the wave reads 64 consecutive blocks (256
+// contiguous bytes); each lane holds all d_I values of its block's pooled key
+// in registers, loaded together.
 // MODE 0: scoring only (the pooled cache is complete).
 // MODE 1, 2: the decode form, where every sequence has at most one new token,
-// so no token of the call needs a row that another token appends.  The kernel
-// then also does the append: workgroup y = 0 of each token writes its K, V and
-// indexer-key rows (read before the position is known), and the workgroup
-// holding the block the token completes pools that block (the new row from
-// kI_new, the older rows from the cache, summed in token order as in
-// append_pool_kernel), scores it from LDS and stores it in the pooled cache.
+// so no token of the call needs a row that another token appends.  Two more
+// workgroups per token (grid y = groups, groups + 1) then do the rest of the
+// step off the scorers' path: the first appends the token's K, V and
+// indexer-key rows (read before the position is known); the second, when the
+// token completes a block, pools that block (the new row from kI_new, the
+// older rows from the cache, summed in token order as in append_pool_kernel),
+// stores it in the pooled cache and writes its score (the scorers skip it).
 // MODE 2: every sequence has exactly one new token (token t is sequence t's),
-// so the pooled keys are read before the position is known as well: one
-// memory round trip for the workgroups that neither append nor pool.
+// so the scorers read the pooled keys before the position is known as well:
+// one memory round trip.
+
+// Score of one pooled key held in LDS (pk[x], x < DI), computed by lane h < HI
+// for head h, then summed over heads by lane 0 in head order: the same fmaf
+// sequence as the scorers' (x ascending per head, then heads ascending).
+template <int HIM, int DI>
+__device__ __forceinline__ float score_one(const Geo& g, const float* qT, const float* wsh,
+                                           const float* pk, float* hsum) {
+  const int lane = threadIdx.x;
+  if (lane < HIM) {
+    float acc = 0.0f;
+    for (int x = 0; x < DI; ++x) acc = fmaf(qT[x * HIM + lane], pk[x], acc);
+    float a = g.idx_scale * acc;
+    hsum[lane] = (a > 0.0f) ? a : 0.0f;
+  }
+  wave_sync();
+  float s = 0.0f;
+  for (int h = 0; h < HIM; ++h)
+    if (h < g.HI) s = fmaf(wsh[h], hsum[h], s);
+  return s;
+}
+
 template <typename E, int HIM, int DI, int MODE>
 __global__ __launch_bounds__(64) void score_kernel(
     Geo g, const E* __restrict__ qI, const float* __restrict__ w, float* __restrict__ pooled,
@@ -268,9 +291,48 @@ __global__ __launch_bounds__(64) void score_kernel(
   constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
   __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
   __shared__ float wsh[HIM];
-  __shared__ float newpool[APPEND ? DI : 1];
   const int t = blockIdx.x, lane = threadIdx.x;
-  const int j = blockIdx.y * 64 + lane;
+  const int groups = (int)gridDim.y - (APPEND ? 2 : 0);
+  const int role = (int)blockIdx.y - groups;  // < 0: scorer; 0: append; 1: pool
+
+  if (APPEND && role == 0) {
+    // This token's new rows, 16 bytes per lane and load (the first 4 per
+    // lane held across the position and page lookups).
+    const int kv_units = 2 * g.Hkv * (g.D / EPV), per = kv_units >> 1, units = g.D / EPV;
+    uint4 kvv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = min(lane + 64 * i, kv_units - 1);
+      const int which = u >= per ? 1 : 0;
+      kvv[i] = *reinterpret_cast<const uint4*>((which ? v_new : k_new) +
+                                               (int64_t)t * g.Hkv * g.D + (u - which * per) * EPV);
+    }
+    const uint4 kiv =
+        *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * DI + min(lane, DI / EPV - 1) * EPV);
+    const QueryPos qp = query_pos(g, t);
+    if (!qp.ok) return;
+    for (int u = lane; u < kv_units; u += 64) {
+      const int which = u >= per ? 1 : 0, rem = u - which * per;
+      const int kvh = rem / units, c = rem - kvh * units;
+      const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
+      if (dst < 0) continue;
+      const int i = (u - lane) >> 6;
+      uint4 v;
+      if (i < 4) {
+        v = kvv[0];
+#pragma unroll
+        for (int ii = 1; ii < 4; ++ii) v = (i == ii) ? kvv[ii] : v;
+      } else {
+        v = *reinterpret_cast<const uint4*>((which ? v_new : k_new) +
+                                            ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV);
+      }
+      *reinterpret_cast<uint4*>((which ? v_cache : k_cache) + dst + c * EPV) = v;
+    }
+    const int64_t drow = idx_row(g, qp.b, qp.p);
+    if (drow >= 0 && lane < DI / EPV) *reinterpret_cast<uint4*>(kI_cache + drow + lane * EPV) = kiv;
+    return;
+  }
+
   // The query and the head weights do not depend on the token's position:
   // staged before the sequence search so the loads overlap.
   {
@@ -281,24 +343,67 @@ __global__ __launch_bounds__(64) void score_kernel(
     }
     if (lane < HIM) wsh[lane] = lane < HI ? w[(int64_t)t * HI + lane] : 0.0f;
   }
-  // Decode form, workgroup 0: this token's new rows, 16 bytes per lane and
-  // load (the first 4 per lane held across the position lookup).
-  const bool appender = APPEND && blockIdx.y == 0;
-  const int kv_units = APPEND ? 2 * g.Hkv * (g.D / EPV) : 0;
-  uint4 kvv[4], kiv = make_uint4(0u, 0u, 0u, 0u);
-  if (appender) {
-    const int per = kv_units >> 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = min(lane + 64 * i, kv_units - 1);
-      const int which = u >= per ? 1 : 0;
-      kvv[i] = *reinterpret_cast<const uint4*>((which ? v_new : k_new) +
-                                               (int64_t)t * g.Hkv * g.D + (u - which * per) * EPV);
+
+  if (APPEND && role == 1) {
+    const QueryPos qp = query_pos(g, t);
+    if (!qp.ok || ((qp.p + 1) & (g.r - 1)) != 0) return;
+    // Rows of the block first (one page lookup per row, all lanes at once;
+    // -2 marks the new row), then chunks of rows staged in LDS with all
+    // loads in flight, then one lane per column adds them in token order.
+    constexpr int UPR = DI / EPV;                        // 16-byte units per row
+    constexpr int RC = 16384 / (DI * (int)sizeof(E));    // rows per staged chunk
+    constexpr int CPT = DI >= 64 ? DI / 64 : 1;          // columns per lane
+    __shared__ int32_t prow[256];  // block_size <= 256
+    __shared__ __attribute__((aligned(16))) E stg[RC * DI];
+    __shared__ float newpool[DI];
+    __shared__ float hsum[HIM];
+    const int nb = (qp.p + 1) >> g.log2r, jnew = nb - 1;
+    const int s0 = jnew << g.log2r;
+    for (int rr = lane; rr < g.r; rr += 64) {
+      const int sr = s0 + rr;
+      const int64_t row = sr == qp.p ? -2 : idx_row(g, qp.b, sr);
+      prow[rr] = row >= 0 ? (int32_t)(row / DI) : (int32_t)row;
     }
-    kiv = *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * DI + min(lane, DI / EPV - 1) * EPV);
+    wave_sync();
+    float acc[CPT];
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) acc[c] = 0.0f;
+    for (int c0 = 0; c0 < g.r; c0 += RC) {
+      const int nrow = min(RC, g.r - c0);
+      for (int u = lane; u < nrow * UPR; u += 64) {
+        const int rr = u / UPR, cc = u - rr * UPR;
+        const int32_t pr = prow[c0 + rr];
+        const E* src = pr == -2 ? kI_new + (int64_t)t * DI : kI_cache + (int64_t)max(pr, 0) * DI;
+        uint4 v = *reinterpret_cast<const uint4*>(src + cc * EPV);
+        if (pr == -1) v = make_uint4(0u, 0u, 0u, 0u);
+        *reinterpret_cast<uint4*>(stg + rr * DI + cc * EPV) = v;
+      }
+      wave_sync();
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int x = lane + 64 * c;
+        if (x < DI)
+          for (int rr = 0; rr < nrow; ++rr) acc[c] = acc[c] + to_f32(stg[rr * DI + x]);
+      }
+      wave_sync();
+    }
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int x = lane + 64 * c;
+      if (x < DI) {
+        newpool[x] = acc[c] * g.inv_r;
+        pooled[((int64_t)qp.b * DI + x) * g.pooled_ld + jnew] = acc[c] * g.inv_r;
+      }
+    }
+    wave_sync();
+    const float sc = score_one<HIM, DI>(g, qT, wsh, newpool, hsum);
+    if (lane == 0 && jnew < g.nbcap) scores[(int64_t)t * g.nbcap + jnew] = sc;
+    return;
   }
-  // The lane's pooled key (unconditional loads at a clamped column).
-  // (Buffer loads: one column offset per lane, the row offset in a scalar.)
+
+  // Scorer.  (Buffer loads: one column offset per lane, the row offset in a
+  // scalar; unconditional, at a clamped column.)
+  const int j = blockIdx.y * 64 + lane;
   float pk[DI];
   auto load_keys = [&](int b) {
     const __amdgpu_buffer_rsrc_t rs =
@@ -315,87 +420,11 @@ __global__ __launch_bounds__(64) void score_kernel(
   if constexpr (!ONEQ) {
     if ((int)blockIdx.y * 64 < nb) load_keys(qp.b);
   }
-  float* srow = scores + (int64_t)t * g.nbcap;
-  int jnew = -1;  // the block this token completes, pooled here
-  if constexpr (APPEND) {
-    if (appender && qp.ok) {
-      const int per = kv_units >> 1, units = g.D / EPV;
-      for (int u = lane; u < kv_units; u += 64) {
-        const int which = u >= per ? 1 : 0, rem = u - which * per;
-        const int kvh = rem / units, c = rem - kvh * units;
-        const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
-        if (dst < 0) continue;
-        uint4 v;
-        const int i = (u - lane) >> 6;
-        if (i < 4) {
-          v = kvv[0];
-#pragma unroll
-          for (int ii = 1; ii < 4; ++ii) v = (i == ii) ? kvv[ii] : v;
-        } else {
-          v = *reinterpret_cast<const uint4*>((which ? v_new : k_new) +
-                                              ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV);
-        }
-        *reinterpret_cast<uint4*>((which ? v_cache : k_cache) + dst + c * EPV) = v;
-      }
-      const int64_t drow = idx_row(g, qp.b, qp.p);
-      if (drow >= 0 && lane < DI / EPV) *reinterpret_cast<uint4*>(kI_cache + drow + lane * EPV) = kiv;
-    }
-    if (qp.ok && ((qp.p + 1) & (g.r - 1)) == 0 && (int)blockIdx.y == (nb - 1) >> 6) {
-      // Rows of the block first (one page lookup per row, all lanes at once;
-      // -2 marks the new row), then chunks of rows staged in LDS with all
-      // loads in flight, then one lane per column adds them in token order.
-      constexpr int UPR = DI / EPV;                        // 16-byte units per row
-      constexpr int RC = 16384 / (DI * (int)sizeof(E));    // rows per staged chunk
-      constexpr int CPT = DI >= 64 ? DI / 64 : 1;          // columns per lane
-      __shared__ int32_t prow[256];  // block_size <= 256
-      __shared__ __attribute__((aligned(16))) E stg[RC * DI];
-      jnew = nb - 1;
-      const int s0 = jnew << g.log2r;
-      for (int rr = lane; rr < g.r; rr += 64) {
-        const int sr = s0 + rr;
-        const int64_t row = sr == qp.p ? -2 : idx_row(g, qp.b, sr);
-        prow[rr] = row >= 0 ? (int32_t)(row / DI) : (int32_t)row;
-      }
-      wave_sync();
-      float acc[CPT];
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) acc[c] = 0.0f;
-      for (int c0 = 0; c0 < g.r; c0 += RC) {
-        const int nrow = min(RC, g.r - c0);
-        for (int u = lane; u < nrow * UPR; u += 64) {
-          const int rr = u / UPR, cc = u - rr * UPR;
-          const int32_t pr = prow[c0 + rr];
-          const E* src = pr == -2 ? kI_new + (int64_t)t * DI : kI_cache + (int64_t)max(pr, 0) * DI;
-          uint4 v = *reinterpret_cast<const uint4*>(src + cc * EPV);
-          if (pr == -1) v = make_uint4(0u, 0u, 0u, 0u);
-          *reinterpret_cast<uint4*>(stg + rr * DI + cc * EPV) = v;
-        }
-        wave_sync();
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int x = lane + 64 * c;
-          if (x < DI)
-            for (int rr = 0; rr < nrow; ++rr) acc[c] = acc[c] + to_f32(stg[rr * DI + x]);
-        }
-        wave_sync();
-      }
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int x = lane + 64 * c;
-        if (x < DI) {
-          newpool[x] = acc[c] * g.inv_r;
-          pooled[((int64_t)qp.b * DI + x) * g.pooled_ld + jnew] = acc[c] * g.inv_r;
-        }
-      }
-    }
-  }
+  // (decode form) the block this token completes is scored by the pooler
+  const int jnew = (APPEND && qp.ok && ((qp.p + 1) & (g.r - 1)) == 0) ? nb - 1 : -1;
   __syncthreads();
   float s = 0.0f;
   if ((int)blockIdx.y * 64 < nb) {
-    if (APPEND && j == jnew) {
-#pragma unroll
-      for (int x = 0; x < DI; ++x) pk[x] = newpool[x];
-    }
     float acc[HIM];
 #pragma unroll
     for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
@@ -438,7 +467,7 @@ __global__ __launch_bounds__(64) void score_kernel(
       }
     }
   }
-  if (j < g.nbcap) srow[j] = (j < nb) ? s : -INFINITY;
+  if (j < g.nbcap && j != jnew) scores[(int64_t)t * g.nbcap + j] = (j < nb) ? s : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -1688,7 +1717,8 @@ hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const voi
 template <typename E, int DI, int MODE>
 void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
               const AppendArgs& ap, hipStream_t st) {
-  dim3 grid(g.T, std::max(1, (g.nbcap + 63) / 64));
+  // (decode form: two more workgroups per token, the appender and the pooler)
+  dim3 grid(g.T, std::max(1, (g.nbcap + 63) / 64) + (MODE != 0 ? 2 : 0));
   const E* q = static_cast<const E*>(qI);
   const E* kn = static_cast<const E*>(ap.k_new);
   const E* vn = static_cast<const E*>(ap.v_new);
