@@ -235,7 +235,15 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
     }
     __syncthreads();
     if (tid < dI) {
-      for (int rr = 0; rr < nrow; ++rr) acc = acc + stage[rr * dI + tid];
+      // (16 rows read at a time so the LDS reads overlap; adds in token order)
+      for (int r0 = 0; r0 < nrow; r0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = stage[min(r0 + i, nrow - 1) * dI + tid];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (r0 + i < nrow) acc = acc + v[i];
+      }
     }
     __syncthreads();
   }
@@ -251,8 +259,9 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
 // MODE 0: scoring only (the pooled cache is complete).
 // MODE 1, 2: the decode form, where every sequence has at most one new token,
 // so no token of the call needs a row that another token appends.  Two more
-// workgroups per token (grid y = groups, groups + 1) then do the rest of the
-// step off the scorers' path: the first appends the token's K, V and
+// workgroups per token (grid y = 0, 1: dispatched first, so that their loads
+// are not queued behind the scorers') do the rest of the step off the
+// scorers' path: the first appends the token's K, V and
 // indexer-key rows (read before the position is known); the second, when the
 // token completes a block, pools that block (the new row from kI_new, the
 // older rows from the cache, summed in token order as in append_pool_kernel),
@@ -270,6 +279,7 @@ __device__ __forceinline__ float score_one(const Geo& g, const float* qT, const 
   const int lane = threadIdx.x;
   if (lane < HIM) {
     float acc = 0.0f;
+#pragma unroll
     for (int x = 0; x < DI; ++x) acc = fmaf(qT[x * HIM + lane], pk[x], acc);
     float a = g.idx_scale * acc;
     hsum[lane] = (a > 0.0f) ? a : 0.0f;
@@ -292,8 +302,9 @@ __global__ __launch_bounds__(64) void score_kernel(
   __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
   __shared__ float wsh[HIM];
   const int t = blockIdx.x, lane = threadIdx.x;
-  const int groups = (int)gridDim.y - (APPEND ? 2 : 0);
-  const int role = (int)blockIdx.y - groups;  // < 0: scorer; 0: append; 1: pool
+  // decode form: y = 0 appends, y = 1 pools, y >= 2 scores group y - 2
+  const int role = APPEND ? (int)blockIdx.y : -1;
+  const int group = APPEND ? (int)blockIdx.y - 2 : (int)blockIdx.y;
 
   if (APPEND && role == 0) {
     // This token's new rows, 16 bytes per lane and load (the first 4 per
@@ -348,13 +359,11 @@ __global__ __launch_bounds__(64) void score_kernel(
     const QueryPos qp = query_pos(g, t);
     if (!qp.ok || ((qp.p + 1) & (g.r - 1)) != 0) return;
     // Rows of the block first (one page lookup per row, all lanes at once;
-    // -2 marks the new row), then chunks of rows staged in LDS with all
-    // loads in flight, then one lane per column adds them in token order.
-    constexpr int UPR = DI / EPV;                        // 16-byte units per row
-    constexpr int RC = 16384 / (DI * (int)sizeof(E));    // rows per staged chunk
-    constexpr int CPT = DI >= 64 ? DI / 64 : 1;          // columns per lane
-    __shared__ int32_t prow[256];  // block_size <= 256
-    __shared__ __attribute__((aligned(16))) E stg[RC * DI];
+    // -2 marks the new row, -1 a row outside the cache), then 64 rows at a
+    // time: every lane loads its column(s) of all 64 rows (all loads in
+    // flight, at addresses chosen by selects), then adds them in token order.
+    constexpr int CPT = DI >= 64 ? DI / 64 : 1;  // columns per lane
+    __shared__ __attribute__((aligned(16))) int32_t prow[256];  // block_size <= 256
     __shared__ float newpool[DI];
     __shared__ float hsum[HIM];
     const int nb = (qp.p + 1) >> g.log2r, jnew = nb - 1;
@@ -365,27 +374,35 @@ __global__ __launch_bounds__(64) void score_kernel(
       prow[rr] = row >= 0 ? (int32_t)(row / DI) : (int32_t)row;
     }
     wave_sync();
+    const E* newrow = kI_new + (int64_t)t * DI;
     float acc[CPT];
 #pragma unroll
     for (int c = 0; c < CPT; ++c) acc[c] = 0.0f;
-    for (int c0 = 0; c0 < g.r; c0 += RC) {
-      const int nrow = min(RC, g.r - c0);
-      for (int u = lane; u < nrow * UPR; u += 64) {
-        const int rr = u / UPR, cc = u - rr * UPR;
-        const int32_t pr = prow[c0 + rr];
-        const E* src = pr == -2 ? kI_new + (int64_t)t * DI : kI_cache + (int64_t)max(pr, 0) * DI;
-        uint4 v = *reinterpret_cast<const uint4*>(src + cc * EPV);
-        if (pr == -1) v = make_uint4(0u, 0u, 0u, 0u);
-        *reinterpret_cast<uint4*>(stg + rr * DI + cc * EPV) = v;
-      }
-      wave_sync();
+    for (int c0 = 0; c0 < g.r; c0 += 64) {
+      const int nrow = min(64, g.r - c0);
+      float v[CPT][64];
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int x = lane + 64 * c;
-        if (x < DI)
-          for (int rr = 0; rr < nrow; ++rr) acc[c] = acc[c] + to_f32(stg[rr * DI + x]);
+      for (int i4 = 0; i4 < 16; ++i4) {
+        const int4 pr4 = *reinterpret_cast<const int4*>(&prow[min(c0 + 4 * i4, 252)]);
+        const int32_t prs[4] = {pr4.x, pr4.y, pr4.z, pr4.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          // (rows past the block read row 0 of the cache and count as zero)
+          const int32_t pr = c0 + 4 * i4 + k < g.r ? prs[k] : -1;
+          const E* src = pr == -2 ? newrow : kI_cache + (int64_t)max(pr, 0) * DI;
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) {
+            const int x = min(lane + 64 * c, DI - 1);
+            const float f = to_f32(src[x]);
+            v[c][4 * i4 + k] = pr == -1 ? 0.0f : f;
+          }
+        }
       }
-      wave_sync();
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+#pragma unroll
+        for (int c = 0; c < CPT; ++c)
+          if (i < nrow) acc[c] = acc[c] + v[c][i];
     }
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -403,7 +420,7 @@ __global__ __launch_bounds__(64) void score_kernel(
 
   // Scorer.  (Buffer loads: one column offset per lane, the row offset in a
   // scalar; unconditional, at a clamped column.)
-  const int j = blockIdx.y * 64 + lane;
+  const int j = group * 64 + lane;
   float pk[DI];
   auto load_keys = [&](int b) {
     const __amdgpu_buffer_rsrc_t rs =
@@ -418,13 +435,13 @@ __global__ __launch_bounds__(64) void score_kernel(
   const QueryPos qp = query_pos(g, t);
   const int nb = qp.ok ? ((qp.p + 1) >> g.log2r) : 0;
   if constexpr (!ONEQ) {
-    if ((int)blockIdx.y * 64 < nb) load_keys(qp.b);
+    if (group * 64 < nb) load_keys(qp.b);
   }
   // (decode form) the block this token completes is scored by the pooler
   const int jnew = (APPEND && qp.ok && ((qp.p + 1) & (g.r - 1)) == 0) ? nb - 1 : -1;
   __syncthreads();
   float s = 0.0f;
-  if ((int)blockIdx.y * 64 < nb) {
+  if (group * 64 < nb) {
     float acc[HIM];
 #pragma unroll
     for (int h = 0; h < HIM; ++h) acc[h] = 0.0f;
