@@ -96,20 +96,27 @@ def main():
         f"min/max {min(case.ctx)}/{max(case.ctx)}")
 
     B, r, k = sp.n_seqs, sp.block_size, sp.k_blocks
+    m = sp.q_per_step          # new tokens (queries) per sequence per step
+    T = B * m
     Hq, Hkv, D, HI, dI = sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads, sp.idx_dim
     esz = 2  # bf16
 
-    # Algorithmic bytes of one step (host formula from positions only).
+    # Algorithmic bytes of one step (host formula from positions only): every
+    # query reads its own selected (or, dense, all) K/V rows.
     def step_bytes(ctx_now):
         kv = idx = 0
         for c in ctx_now:
-            n = c + 1
-            nb = n // r
-            nsel = r * min(k, nb) + (n - r * nb)
-            kv += nsel * Hkv * D * esz * 2
-            idx += nb * dI * 4                      # pooled keys read by the scorer
-        qgo = B * Hq * D * esz * 3 + B * (HI * dI * esz + HI * 4)
-        new_rows = B * (2 * Hkv * D + dI) * esz
+            for i in range(m):
+                n = c + i + 1
+                if r > 0:
+                    nb = n // r
+                    nsel = r * min(k, nb) + (n - r * nb)
+                    idx += nb * dI * 4              # pooled keys read by the scorer
+                else:
+                    nsel = n
+                kv += nsel * Hkv * D * esz * 2
+        qgo = T * Hq * D * esz * 3 + (T * (HI * dI * esz + HI * 4) if r > 0 else 0)
+        new_rows = T * (2 * Hkv * D + (dI if r > 0 else 0)) * esz
         return kv, idx, qgo + new_rows
 
     kv0, idx0, small0 = step_bytes(case.ctx)
@@ -118,7 +125,7 @@ def main():
     total = args.warmup + args.steps
     per_layer_steps = math.ceil(total / L) + 1
     t0 = time.time()
-    dc = runner.DeviceCase(case, device=dev, n_layers=L, extra_steps=per_layer_steps)
+    dc = runner.DeviceCase(case, device=dev, n_layers=L, extra_steps=per_layer_steps * m)
     log(f"[bench] {L} layer copies on the GPU in {time.time() - t0:.1f}s "
         f"({per_step / 1e6:.1f} MB algorithmic per step)")
 
@@ -132,18 +139,20 @@ def main():
 
     steps_in = []
     for s in range(total):
-        steps_in.append({
-            "q": nrm((B, Hq, D), D ** -0.5), "k_new": nrm((B, Hkv, D), D ** -0.5),
-            "v_new": nrm((B, Hkv, D), D ** -0.5), "qI": nrm((B, HI, dI), dI ** -0.5),
-            "kI_new": nrm((B, dI), dI ** -0.5),
-            "w": torch.rand((B, HI), generator=gen, device=dev),
-            "gate": nrm((B, Hq, D), 1.0)})
-    batches = [dc.batch_for([c + j for c in case.ctx], [1] * B) for j in range(per_layer_steps)]
+        x = {"q": nrm((T, Hq, D), D ** -0.5), "k_new": nrm((T, Hkv, D), D ** -0.5),
+             "v_new": nrm((T, Hkv, D), D ** -0.5), "gate": nrm((T, Hq, D), 1.0),
+             "qI": None, "kI_new": None, "w": None}
+        if r > 0:
+            x.update({"qI": nrm((T, HI, dI), dI ** -0.5), "kI_new": nrm((T, dI), dI ** -0.5),
+                      "w": torch.rand((T, HI), generator=gen, device=dev)})
+        steps_in.append(x)
+    batches = [dc.batch_for([c + j * m for c in case.ctx], [m] * B)
+               for j in range(per_layer_steps)]
     ws_bytes = max(qsa.qsa_workspace_size(dc.params, bt) for bt in batches)
     ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
-    outs = [torch.empty((B, Hq, D), dtype=bf, device=dev) for _ in range(total)]
-    sels = [torch.empty((B, k), dtype=torch.int32, device=dev) for _ in range(total)]
-    nbls = [torch.empty((B,), dtype=torch.int32, device=dev) for _ in range(total)]
+    outs = [torch.empty((T, Hq, D), dtype=bf, device=dev) for _ in range(total)]
+    sels = [torch.empty((T, max(k, 1)), dtype=torch.int32, device=dev) for _ in range(total)]
+    nbls = [torch.empty((T,), dtype=torch.int32, device=dev) for _ in range(total)]
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -151,8 +160,8 @@ def main():
         l, j = s % L, s // L
         st, x = dc.layers[l], steps_in[s]
         qsa.qsa_forward(dc.params, batches[j], x["q"], x["k_new"], x["v_new"], x["qI"],
-                        x["kI_new"], x["w"], x["gate"], st["k"], st["v"], st["kI"],
-                        st["pooled"], outs[s], sels[s], nbls[s], ws, sh)
+                        x["kI_new"], x["w"], x["gate"], st["k"], st["v"], st.get("kI"),
+                        st.get("pooled"), outs[s], sels[s], nbls[s], ws, sh)
 
     for s in range(args.warmup):
         fwd(s)
@@ -164,7 +173,7 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize(dev)
     ms_step = e0.elapsed_time(e1) / args.steps
-    tok_s = B / (ms_step * 1e-3)
+    tok_s = T / (ms_step * 1e-3)
     hbm_gbps = per_step / (ms_step * 1e-3) / 1e9
 
     # Dominant kernel: the attention of each timed step, launched alone on the
@@ -180,7 +189,7 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize(dev)
     attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    attn_bytes = kv0 + B * Hq * D * esz * 3
+    attn_bytes = kv0 + T * Hq * D * esz * 3
     attn_gbps = attn_bytes / (attn_ms * 1e-3) / 1e9
 
     res = {
@@ -190,7 +199,7 @@ def main():
         "data": ("synthetic (seeded; " + (f"contexts U[{sp.ctx_lo},{sp.ctx_hi}]" if sp.ctx_hi
                                           else f"context {sp.ctx}") +
                  "; N(0,1)/sqrt(d) q/k/v; decode inputs drawn on the GPU)"),
-        "config": {"workload": name, "batch": B, "ctx_min": min(case.ctx),
+        "config": {"workload": name, "batch": B, "q_per_step": m, "ctx_min": min(case.ctx),
                    "ctx_max": max(case.ctx), "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "block_size": r, "budget": sp.budget,
                    "idx_heads": HI, "idx_dim": dI, "paged": bool(sp.page_size),
@@ -339,11 +348,13 @@ def cpu_baseline(case, sp, seconds):
     f32 = [(workloads.as_f32(case.k[b]), workloads.as_f32(case.v[b]),
             workloads.as_f32(case.kI[b])) for b in range(B)]
 
+    m = sp.q_per_step
+
     def one(b):
         K, V, kI = f32[b]
         p = case.ctx[b]
-        orc.sequence(dims, K, V, kI, np.array([p]), case.q[b][:1], case.qI[b][:1],
-                     case.w[b][:1], case.gate[b][:1])
+        orc.sequence(dims, K, V, kI, np.arange(p, p + m), case.q[b][:m], case.qI[b][:m],
+                     case.w[b][:m], case.gate[b][:m])
 
     threads = min(cores, B)
     reps = 0
@@ -355,10 +366,10 @@ def cpu_baseline(case, sp, seconds):
             if time.time() - t0 >= seconds:
                 break
     dt = time.time() - t0
-    return {"value": round(reps * B / dt, 2), "unit": "tok/s", "cores": threads,
+    return {"value": round(reps * B * m / dt, 2), "unit": "tok/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{reps} x one decode step of all {B} sequences (the same inputs), "
-                      f"threads over sequences, {dt:.1f}s wall",
+            "sample": f"{reps} x one decode step of all {B} sequences ({m} new token(s) "
+                      f"each, the same inputs), threads over sequences, {dt:.1f}s wall",
             "cpu_model": _cpu_model()}
 
 

@@ -18,7 +18,8 @@ Recipe (every workload, one seed):
   even, through torch on the CPU); both sides see the same rounded bits
   (stored here as uint16).
 * Decode workloads: a sequence holds ``ctx`` cached tokens (positions
-  0..ctx-1) and each step appends one new token, which is also the query.
+  0..ctx-1) and each step appends ``q_per_step`` new tokens (one, or several
+  for speculative verification), which are also the queries.
   Prefill workloads: every token is a query; tokens arrive in chunks.
 
 The five workloads follow the QSA description on the Qwen4-Exp pages (MTPLX
@@ -62,6 +63,7 @@ class Spec:
     ctx_lo: int = 0
     ctx_hi: int = 0
     steps: int = 1
+    q_per_step: int = 1       # decode: new tokens per sequence per call (speculative verify)
     # paged KV (0 = contiguous)
     page_size: int = 0
     # planting
@@ -71,7 +73,7 @@ class Spec:
 
     @property
     def k_blocks(self) -> int:
-        return self.budget // self.block_size
+        return self.budget // self.block_size if self.block_size > 0 else 0
 
 
 SPECS: Dict[str, Spec] = {
@@ -98,6 +100,21 @@ SPECS: Dict[str, Spec] = {
         name="long_decode_256k_bf16", kind="decode", dtype=BF16, n_seqs=4,
         n_q_heads=32, n_kv_heads=4, head_dim=128, n_idx_heads=8, idx_dim=64,
         block_size=128, budget=4096, ctx=262144, steps=128, planted=64),
+    # Beyond the five configurations: speculative decoding.  A draft head
+    # proposes tokens that the QSA layers then verify in one call per
+    # sequence (several new tokens, each its own query with its own causal
+    # selection), and the draft head's own layer attends densely (block size
+    # 0).  Same batch, contexts and paging as the ragged decode.
+    "spec_verify_ragged_bf16": Spec(
+        name="spec_verify_ragged_bf16", kind="decode", dtype=BF16, n_seqs=32,
+        n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,
+        block_size=64, budget=4096, ctx_lo=8192, ctx_hi=131072, steps=1,
+        q_per_step=4, page_size=64),
+    "mtp_dense_ragged_bf16": Spec(
+        name="mtp_dense_ragged_bf16", kind="decode", dtype=BF16, n_seqs=32,
+        n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,
+        block_size=0, budget=0, ctx_lo=8192, ctx_hi=131072, steps=1,
+        page_size=64),
 }
 
 ORDER = ["tiny_prefill_f32", "decode_32k_bf16", "chunked_prefill_32k_bf16",
@@ -211,7 +228,7 @@ def _draw(sp: Spec, seed: int) -> Case:
             ctx = [int(x) for x in meta_rng.integers(sp.ctx_lo, sp.ctx_hi + 1, size=B)]
         else:
             ctx = [sp.ctx] * B
-        n_new = [sp.steps] * B
+        n_new = [sp.steps * sp.q_per_step] * B
     n_tok = [c + n for c, n in zip(ctx, n_new)]
 
     # Per-sequence tensor streams.
@@ -228,7 +245,7 @@ def _draw(sp: Spec, seed: int) -> Case:
         w = rngs[5].random((nq, sp.n_idx_heads), dtype=np.float32)
         gate = _normal(rngs[6], (nq, sp.n_q_heads, D), 1.0, sp.dtype)
         # Planted high-relevance blocks among this sequence's complete blocks.
-        nblk = n // r
+        nblk = n // r if r > 0 else 0
         prng = rngs[7]
         if sp.planted_density > 0:
             npl = int(round(sp.planted_density * nblk))
@@ -261,8 +278,9 @@ def _draw(sp: Spec, seed: int) -> Case:
         for s in range(0, sp.prefill_len, ch):
             calls.append([(s, min(s + ch, sp.prefill_len))] * B)
     else:
+        m = sp.q_per_step
         for i in range(sp.steps):
-            calls.append([(ctx[b] + i, ctx[b] + i + 1) for b in range(B)])
+            calls.append([(ctx[b] + i * m, ctx[b] + (i + 1) * m) for b in range(B)])
 
     page_table = None
     n_pages = 0

@@ -110,6 +110,28 @@ def test_paged_cache_over_4gib():
     torch.cuda.empty_cache()
 
 
+def test_spec_verify_paged_several_tokens_per_call():
+    """Speculative verification: each call appends 4 tokens per sequence on a
+    paged cache (each its own query with its own selection); every sequence
+    completes blocks inside a call, and the pooled cache equals from-scratch
+    pooling at the end."""
+    case = workloads.make_case("spec_verify_ragged_bf16", n_seqs=5, ctx_range=(3000, 9000),
+                               steps=20)
+    dc, _, _ = _full(case, keep={0, 1, 9, 19})
+    orc = oracle.load()
+    got = pooled_rows(dc)
+    for b in range(case.spec.n_seqs):
+        ref = orc.pool(case.kI[b], case.spec.block_size)
+        assert np.array_equal(got[b, :ref.shape[0]], ref)
+
+
+def test_dense_draft_layer_paged_decode():
+    """The draft head's dense layer (block size 0) decoding over ragged paged
+    contexts."""
+    _full(workloads.make_case("mtp_dense_ragged_bf16", n_seqs=4, ctx_range=(2000, 7000),
+                              steps=2))
+
+
 def test_dense_long_context_several_rounds():
     """A dense layer over 140000 cached tokens: each split holds more list
     positions than one round of row resolution."""
