@@ -1244,13 +1244,15 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
 
   for (int r0 = i0; r0 < i1; r0 += RR) {
-    if (r0 != i0) {
-      fetch_sel(r0);
-      fetch_pages(r0);
-    }
     __syncthreads();  // the previous round's rows are no longer read
     resolve_round(r0);
     __syncthreads();  // rows (and, the first time, the query) visible
+    // The next round's selection entries and pages are requested now, so
+    // their latency hides behind this round's tiles.
+    if (r0 + RR < i1) {
+      fetch_sel(r0 + RR);
+      fetch_pages(r0 + RR);
+    }
     const int r1 = min(r0 + RR, i1);
     uint4 kr[4][4];          // [token group][dim step]: A operands
     uint2 vr[32];            // tokens 32*half + j, dims 4*c32 .. +3
