@@ -530,10 +530,12 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* sh) {
 __device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb, int jn, int k,
                                                  int32_t* out) {
   // Two histograms: while wave 0 scans one, the other is cleared for the next
-  // pass, so a pass costs two barriers.
+  // pass, so a pass costs two barriers.  The passes stop early once the keys
+  // that share the digits found so far are exactly the ones still wanted:
+  // then all of them are kept, whatever their lower bits.
   __shared__ __attribute__((aligned(16))) uint32_t hist[2][256];
   __shared__ uint32_t s_prefix;
-  __shared__ int s_want;
+  __shared__ int s_want, s_cnt;
   __shared__ int sh[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   uint32_t prefix = 0, mask = 0;
@@ -558,6 +560,7 @@ __device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb
         if (above < want && above + c[i] >= want) {
           s_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
           s_want = want - above;
+          s_cnt = c[i];
         }
         above += c[i];
       }
@@ -567,15 +570,17 @@ __device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb
     prefix = s_prefix;
     want = s_want;
     mask |= 255u << shift;
+    if (s_cnt == want) break;  // (the same value in every thread)
   }
-  // Keep keys > prefix, and the first `want` keys == prefix in index order:
-  // one packed scan gives each thread both counts before it.
+  // Keep keys above the found digits, and the first `want` keys that share
+  // them in index order: one packed scan gives each thread both counts.
   int n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < jn) {
-      n_gt += kr[e] > prefix ? 1 : 0;
-      n_eq += kr[e] == prefix ? 1 : 0;
+      const uint32_t km = kr[e] & mask;
+      n_gt += km > prefix ? 1 : 0;
+      n_eq += km == prefix ? 1 : 0;
     }
   }
   int tot;
@@ -585,8 +590,9 @@ __device__ __forceinline__ void block_radix_topk(const uint32_t (&kr)[8], int jb
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < jn) {
-      const bool eq = kr[e] == prefix;
-      if (kr[e] > prefix || (eq && eqr < want)) {
+      const uint32_t km = kr[e] & mask;
+      const bool eq = km == prefix;
+      if (km > prefix || (eq && eqr < want)) {
         if (pos < k) out[pos] = jb + e;
         ++pos;
       }
