@@ -69,8 +69,54 @@ class Oracle:
             C.POINTER(C.c_float), C.POINTER(C.c_int32), C.POINTER(C.c_int32),
             C.POINTER(C.c_int64), C.POINTER(C.c_float), C.c_int64]
 
+        L.qsa_oracle_e4m3_decode.restype = C.c_float
+        L.qsa_oracle_e4m3_decode.argtypes = [C.c_uint8]
+        L.qsa_oracle_e4m3_encode.restype = C.c_uint8
+        L.qsa_oracle_e4m3_encode.argtypes = [C.c_float]
+        L.qsa_oracle_fwht.restype = None
+        L.qsa_oracle_fwht.argtypes = [C.POINTER(C.c_float), C.c_int32]
+        L.qsa_oracle_kv8_encode.restype = None
+        L.qsa_oracle_kv8_encode.argtypes = [C.POINTER(C.c_float), C.c_int64, C.c_int32, C.c_int32,
+                                            C.c_float, C.POINTER(C.c_uint8)]
+        L.qsa_oracle_sequence_kv8.restype = C.c_int
+        L.qsa_oracle_sequence_kv8.argtypes = [
+            C.POINTER(Dims), C.c_int64, C.POINTER(C.c_uint8), C.POINTER(C.c_uint8), C.c_int32,
+            C.c_float, C.c_float, C.POINTER(C.c_float), C.c_int64, C.POINTER(C.c_int64),
+            C.POINTER(C.c_float), C.POINTER(C.c_float), C.POINTER(C.c_float),
+            C.POINTER(C.c_float), C.POINTER(C.c_float), C.POINTER(C.c_int32),
+            C.POINTER(C.c_int32), C.POINTER(C.c_int64), C.POINTER(C.c_float), C.c_int64]
+
     def threads(self) -> int:
         return int(self._L.qsa_oracle_threads())
+
+    # --- 8-bit K/V storage ----------------------------------------------------
+    def e4m3_decode(self, codes) -> np.ndarray:
+        codes = np.asarray(codes, np.uint8)
+        f = self._L.qsa_oracle_e4m3_decode
+        return np.array([f(int(c)) for c in codes.ravel()], np.float32).reshape(codes.shape)
+
+    def e4m3_encode(self, x) -> np.ndarray:
+        x = np.asarray(x, np.float32)
+        f = self._L.qsa_oracle_e4m3_encode
+        return np.array([f(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+    def fwht(self, x) -> np.ndarray:
+        x = np.array(x, np.float32, copy=True)
+        n = x.shape[-1]
+        flat = np.ascontiguousarray(x.reshape(-1, n))
+        for row in flat:
+            self._L.qsa_oracle_fwht(_p(row), n)
+        return flat.reshape(x.shape)
+
+    def kv8_encode(self, x, rotate: bool, inv_scale: float) -> np.ndarray:
+        """Storage codes of rows [..., D] (see qsa_oracle_kv8_encode)."""
+        x = _f32(x)
+        D = x.shape[-1]
+        flat = np.ascontiguousarray(x.reshape(-1, D))
+        codes = np.zeros(flat.shape, np.uint8)
+        self._L.qsa_oracle_kv8_encode(_p(flat), flat.shape[0], D, int(rotate), inv_scale,
+                                      _p(codes, C.c_uint8))
+        return codes.reshape(x.shape)
 
     # --- single steps -------------------------------------------------------
     def pool(self, kI, r: int) -> np.ndarray:
@@ -116,6 +162,43 @@ class Oracle:
         return out
 
     # --- whole QSA over the queries of one sequence --------------------------
+    def sequence_kv8(self, dims: dict, Kc, Vc, rotate: bool, k_scale: float, v_scale: float,
+                     kI, pos, q, qI, w, gate, want_scores: bool = False,
+                     nb_cap: Optional[int] = None) -> dict:
+        """As ``sequence``, with K and V stored as 8-bit codes Kc, Vc
+        [n_tok, Hkv, D] (uint8) and scales; see qsa_oracle_sequence_kv8."""
+        d = Dims(**{f: dims.get(f, 0) for f, _ in Dims._fields_})
+        Kc = np.ascontiguousarray(Kc, np.uint8)
+        Vc = np.ascontiguousarray(Vc, np.uint8)
+        n_tok = Kc.shape[0]
+        kI = _f32(kI) if kI is not None else np.zeros((n_tok, 1), np.float32)
+        pos = np.ascontiguousarray(pos, np.int64)
+        nq = pos.size
+        Hq, D, HI = d.n_q_heads, d.head_dim, max(d.n_idx_heads, 1)
+        q, gate = _f32(q).reshape(nq, Hq, D), _f32(gate).reshape(nq, Hq, D)
+        qI = _f32(qI).reshape(nq, HI, -1) if qI is not None else np.zeros((nq, 1, 1), np.float32)
+        w = _f32(w).reshape(nq, HI) if w is not None else np.zeros((nq, 1), np.float32)
+        r = d.block_size
+        k = d.budget // r if r > 0 else 0
+        out = np.zeros((nq, Hq, D), np.float32)
+        sel = np.full((nq, max(k, 1)), -1, np.int32)
+        nblk = np.zeros(nq, np.int32)
+        ntok = np.zeros(nq, np.int64)
+        if nb_cap is None:
+            nb_cap = (n_tok // r) if r > 0 else 0
+        scores = np.zeros((nq, max(nb_cap, 1)), np.float32) if want_scores else None
+        rc = self._L.qsa_oracle_sequence_kv8(
+            C.byref(d), n_tok, _p(Kc, C.c_uint8), _p(Vc, C.c_uint8), int(rotate), k_scale,
+            v_scale, _p(kI), nq, _p(pos, C.c_int64), _p(q), _p(qI), _p(w), _p(gate), _p(out),
+            _p(sel, C.c_int32), _p(nblk, C.c_int32), _p(ntok, C.c_int64), _p(scores), nb_cap)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        res = {"out": out, "sel": sel[:, :k] if k else sel[:, :0], "n_blocks": nblk,
+               "n_tokens": ntok}
+        if want_scores:
+            res["scores"] = scores[:, :nb_cap]
+        return res
+
     def sequence(self, dims: dict, K, V, kI, pos, q, qI, w, gate, want_scores: bool = False,
                  nb_cap: Optional[int] = None) -> dict:
         """QSA outputs of the queries at positions ``pos`` of one sequence.

@@ -165,7 +165,7 @@ int64_t qsa_oracle_token_set(const int32_t* sel, int32_t n_sel, int32_t r, int64
  * QSA section: "standard gated GQA"; LocalAI commit: gather consumer, then
  * the sigmoid output gate).  K, V: [n_tok][Hkv][D].  For head h, KV head
  * h / (Hq/Hkv); z_t = scale * <q_h, K_t>; softmax over the list; o = sum p V;
- * out = o * sigmoid(gate), elementwise.  fp64 accumulation. */
+ * out = o * sigmoid(gate), elementwise (gate NULL: no gate).  fp64 accumulation. */
 void qsa_oracle_attend(const float* q, const float* K, const float* V, const float* gate,
                        const int64_t* tokens, int64_t n_t, int32_t Hq, int32_t Hkv, int32_t D,
                        double scale, float* out) {
@@ -192,7 +192,7 @@ void qsa_oracle_attend(const float* q, const float* K, const float* V, const flo
       for (int32_t x = 0; x < D; ++x) o[x] += e * (double)vr[x];
     }
     for (int32_t x = 0; x < D; ++x) {
-      double gt = 1.0 / (1.0 + exp(-(double)gate[(int64_t)h * D + x]));
+      double gt = gate ? 1.0 / (1.0 + exp(-(double)gate[(int64_t)h * D + x])) : 1.0;
       out[(int64_t)h * D + x] = (float)(o[x] / l * gt);
     }
   }
@@ -263,11 +263,133 @@ int qsa_oracle_sequence(const qsa_oracle_dims* dm, int64_t n_tok, const float* K
     int64_t nt = qsa_oracle_token_set(sl, nsel, r, p, toks);
     if (n_blocks) n_blocks[i] = nsel;
     if (n_tokens) n_tokens[i] = nt;
-    qsa_oracle_attend(q + i * Hq * D, K, V, gate + i * Hq * D, toks, nt, Hq, Hkv, D, a_scale,
+    qsa_oracle_attend(q + i * Hq * D, K, V, gate ? gate + i * Hq * D : NULL, toks, nt, Hq, Hkv,
+                      D, a_scale,
                       out + i * Hq * D);
     free(sl);
     free(toks);
   }
   free(pooled);
+  return rc;
+}
+
+/* ---------------------------------------------------------------------------
+ * K/V stored as 8-bit floats, optionally in a Walsh-Hadamard-rotated basis.
+ *
+ * "Porting Qwen4 to llama.cpp", section "Quantized KV Is a Representation
+ * Contract": quantized K/V may be kept in a rotated basis H; with Q' = HQ and
+ * K' = HK the scores are unchanged for orthonormal H, and a QSA attention
+ * path has to honour the same storage contract as the dense path (rotate
+ * before the cache write, un-rotate the output).  Here H is the Sylvester
+ * Hadamard matrix of order D with entries +-1 (H H = D I), so the scores of
+ * the rotated vectors carry a factor D and the output of the rotated values
+ * is un-rotated as H o' / D.
+ *
+ * The 8-bit format is OCP E4M3 ("fn"): 1 sign bit, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent 0 is subnormal (m * 2^-9); no
+ * infinities; S.1111.111 is NaN, so the largest finite value is 448.  A
+ * stored code c with scale s stands for decode(c) * s.  Encoding rounds to
+ * the nearest code, ties to the even code, and saturates at +-448.
+ */
+float qsa_oracle_e4m3_decode(uint8_t c) {
+  const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return NAN;
+  const float v = (e == 0) ? ldexpf((float)m, -9) : ldexpf((float)(8 + m), e - 10);
+  return sgn ? -v : v;
+}
+
+/* Nearest finite code by direct search over the 127 non-negative codes
+ * (their values increase with the code); ties go to the even code. */
+uint8_t qsa_oracle_e4m3_encode(float x) {
+  if (isnan(x)) return 0x7F;
+  const uint8_t sgn = signbit(x) ? 0x80 : 0x00;
+  const float a = fabsf(x);
+  if (a >= 448.0f) return sgn | 0x7E;
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    const double d = fabs((double)qsa_oracle_e4m3_decode((uint8_t)c) - (double)a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return sgn | (uint8_t)best;
+}
+
+/* In-place Walsh-Hadamard transform of x[0..n), n a power of two: H_n x with
+ * the Sylvester H_n (entries +-1, no normalisation), in the standard order of
+ * butterflies: for len = 1, 2, 4, ...: (x[j], x[j+len]) <- (x[j] + x[j+len],
+ * x[j] - x[j+len]).  fp32. */
+void qsa_oracle_fwht(float* x, int32_t n) {
+  for (int32_t len = 1; len < n; len <<= 1)
+    for (int32_t i = 0; i < n; i += 2 * len)
+      for (int32_t j = i; j < i + len; ++j) {
+        const float a = x[j], b = x[j + len];
+        x[j] = a + b;
+        x[j + len] = a - b;
+      }
+}
+
+/* Storage codes of `rows` rows of D values: (rotate ? H x : x) * inv_scale,
+ * encoded.  inv_scale is the fp32 reciprocal of the scale (1.0f / s). */
+void qsa_oracle_kv8_encode(const float* x, int64_t rows, int32_t D, int32_t rotate,
+                           float inv_scale, uint8_t* codes) {
+  float* t = (float*)malloc(sizeof(float) * (size_t)D);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int32_t i = 0; i < D; ++i) t[i] = x[r * D + i];
+    if (rotate) qsa_oracle_fwht(t, D);
+    for (int32_t i = 0; i < D; ++i) codes[r * D + i] = qsa_oracle_e4m3_encode(t[i] * inv_scale);
+  }
+  free(t);
+}
+
+/* QSA over K/V stored as 8-bit codes (the storage above), for nq queries of
+ * one sequence: as qsa_oracle_sequence, with K and V given by their codes
+ * Kc, Vc [n_tok][Hkv][D] and scales.  The selection does not involve K/V.
+ * With rotate, the query is rotated (q' = H q), the attention scale is
+ * divided by D, and the gate-free output o' is un-rotated (H o' / D) before
+ * the gate. */
+int qsa_oracle_sequence_kv8(const qsa_oracle_dims* dm, int64_t n_tok, const uint8_t* Kc,
+                            const uint8_t* Vc, int32_t rotate, float k_scale, float v_scale,
+                            const float* kI, int64_t nq, const int64_t* pos, const float* q,
+                            const float* qI, const float* w, const float* gate, float* out,
+                            int32_t* sel, int32_t* n_blocks, int64_t* n_tokens, float* scores,
+                            int64_t nb_cap) {
+  const int32_t Hq = dm->n_q_heads, Hkv = dm->n_kv_heads, D = dm->head_dim;
+  if (Hq <= 0 || Hkv <= 0 || D <= 0) return -1;
+  const int64_t nkv = n_tok * Hkv * D, nqv = nq * Hq * D;
+  float* Kd = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1));
+  float* Vd = (float*)malloc(sizeof(float) * (size_t)(nkv > 0 ? nkv : 1));
+  float* qr = (float*)malloc(sizeof(float) * (size_t)(nqv > 0 ? nqv : 1));
+  for (int64_t i = 0; i < nkv; ++i) {
+    Kd[i] = qsa_oracle_e4m3_decode(Kc[i]) * k_scale;
+    Vd[i] = qsa_oracle_e4m3_decode(Vc[i]) * v_scale;
+  }
+  for (int64_t i = 0; i < nqv; ++i) qr[i] = q[i];
+  qsa_oracle_dims d2 = *dm;
+  const double a_scale = dm->attn_scale > 0.0f ? (double)dm->attn_scale : 1.0 / sqrt((double)D);
+  if (rotate) {
+    for (int64_t i = 0; i < nq * Hq; ++i) qsa_oracle_fwht(qr + i * D, D);
+    d2.attn_scale = (float)(a_scale / (double)D);
+  }
+  const int rc = qsa_oracle_sequence(&d2, n_tok, Kd, Vd, kI, nq, pos, qr, qI, w, NULL, out, sel,
+                                     n_blocks, n_tokens, scores, nb_cap);
+  if (rc == 0) {
+    for (int64_t i = 0; i < nq * Hq; ++i) {
+      float* o = out + i * D;
+      if (rotate) {
+        qsa_oracle_fwht(o, D);
+        for (int32_t x = 0; x < D; ++x) o[x] = o[x] / (float)D;
+      }
+      for (int32_t x = 0; x < D; ++x) {
+        const double gt = 1.0 / (1.0 + exp(-(double)gate[i * D + x]));
+        o[x] = (float)((double)o[x] * gt);
+      }
+    }
+  }
+  free(Kd);
+  free(Vd);
+  free(qr);
   return rc;
 }

@@ -365,9 +365,106 @@ def pin_planted_selected(o):
                      q[-1:], qI[-1:], w[-1:], gate[-1:])
     assert set(planted) <= set(res["sel"][0].tolist())
 
+# ------------------------------------------------ 8-bit K/V storage contract
+def pin_e4m3_decode_matches_torch(o):
+    """Every one of the 256 codes decodes to torch's float8_e4m3fn value (the
+    OCP E4M3 format), NaN codes included."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = o.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    both_nan = np.isnan(got) & np.isnan(ref)
+    assert np.all((got == ref) | both_nan)
+    assert np.array_equal(np.signbit(got[~both_nan]), np.signbit(ref[~both_nan]))
+
+
+def pin_e4m3_encode_rounding(o):
+    """Encoding is round-to-nearest-even to the finite codes: it inverts the
+    decoding on every finite code, agrees with torch's float8_e4m3fn
+    conversion on random values and on every midpoint between neighbouring
+    codes (ties to the even code), and saturates at +-448."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = o.e4m3_decode(codes)
+    assert np.array_equal(o.e4m3_encode(vals), codes)
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.standard_normal(3000) * 30, rng.standard_normal(1000) * 0.01,
+                        rng.uniform(-440, 440, 500)]).astype(np.float32)
+    pos = np.sort(np.unique(o.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))))
+    mids = ((pos[:-1].astype(np.float64) + pos[1:]) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (pos[:-1].astype(np.float64) + pos[1:]) / 2)
+    x = np.concatenate([x, mids, -mids])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(o.e4m3_encode(x), ref)
+    big = np.array([448.0, 449.0, 470.0, 1e6, -500.0], np.float32)
+    assert np.array_equal(o.e4m3_encode(big), np.array([0x7E, 0x7E, 0x7E, 0x7E, 0xFE], np.uint8))
+
+
+def pin_fwht_is_sylvester_hadamard(o):
+    """The transform is multiplication by the Sylvester Hadamard matrix
+    (H_1 = [1], H_2n = [[H, H], [H, -H]]): exact on small integers, and
+    applying it twice multiplies by n."""
+    for n in (2, 8, 128):
+        H = np.array([[1.0]])
+        while H.shape[0] < n:
+            H = np.block([[H, H], [H, -H]])
+        rng = np.random.default_rng(n)
+        x = rng.integers(-8, 9, size=(5, n)).astype(np.float32)
+        assert np.array_equal(o.fwht(x), (x.astype(np.float64) @ H.T).astype(np.float32))
+        assert np.array_equal(o.fwht(o.fwht(x)), x * n)
+
+
+def pin_kv8_storage_is_transparent_when_exact(o):
+    """With K/V whose stored form is exact (values on the 8-bit grid; with
+    rotation, K = H e / D and V = H f / D for small integers e, f, so the
+    rotated rows are the integers themselves), QSA over the 8-bit storage
+    equals QSA over the plain K/V: the rotation of the query, the 1/D on the
+    scores and the un-rotation of the output cancel exactly as the storage
+    contract says."""
+    rng = np.random.default_rng(41)
+    Hq, Hkv, D, HI, dI, r, budget, n = 4, 2, 32, 2, 16, 8, 48, 200
+    _, _, kI, q, qI, w, gate = _rand_seq(rng, n, Hq, Hkv, D, HI, dI)
+    dims = _dims(Hq, Hkv, D, HI, dI, r, budget)
+    pos = np.array([37, 120, n - 1])
+    # no rotation: values on the grid (multiples of 1/8 times a power of two scale)
+    scale = 0.25
+    Kg = (rng.integers(-15, 16, size=(n, Hkv, D)) / 8.0 * scale).astype(np.float32)
+    Vg = (rng.integers(-15, 16, size=(n, Hkv, D)) / 8.0 * scale).astype(np.float32)
+    Kc = o.kv8_encode(Kg, False, 1.0 / scale)
+    Vc = o.kv8_encode(Vg, False, 1.0 / scale)
+    assert np.array_equal(o.e4m3_decode(Kc) * np.float32(scale), Kg)
+    a = o.sequence_kv8(dims, Kc, Vc, False, scale, scale, kI, pos, q[pos], qI[pos], w[pos],
+                       gate[pos])
+    b = o.sequence(dims, Kg, Vg, kI, pos, q[pos], qI[pos], w[pos], gate[pos])
+    assert np.array_equal(a["sel"], b["sel"])
+    assert np.allclose(a["out"], b["out"], rtol=1e-5, atol=1e-6)
+    # different scales for K and V
+    Vh = (Vg * np.float32(2.0)).astype(np.float32)
+    a = o.sequence_kv8(dims, Kc, o.kv8_encode(Vh, False, 1.0 / (2 * scale)), False, scale,
+                       2 * scale, kI, pos, q[pos], qI[pos], w[pos], gate[pos])
+    b = o.sequence(dims, Kg, Vh, kI, pos, q[pos], qI[pos], w[pos], gate[pos])
+    assert np.allclose(a["out"], b["out"], rtol=1e-5, atol=1e-6)
+    # rotation: the rotated rows are small integers
+    e = rng.integers(-6, 7, size=(n, Hkv, D)).astype(np.float32)
+    f = rng.integers(-6, 7, size=(n, Hkv, D)).astype(np.float32)
+    Kr = o.fwht(e) / np.float32(D)
+    Vr = o.fwht(f) / np.float32(D)
+    Kc = o.kv8_encode(Kr, True, 1.0)
+    Vc = o.kv8_encode(Vr, True, 1.0)
+    assert np.array_equal(o.e4m3_decode(Kc), e) and np.array_equal(o.e4m3_decode(Vc), f)
+    a = o.sequence_kv8(dims, Kc, Vc, True, 1.0, 1.0, kI, pos, q[pos], qI[pos], w[pos],
+                       gate[pos])
+    b = o.sequence(dims, Kr, Vr, kI, pos, q[pos], qI[pos], w[pos], gate[pos])
+    assert np.array_equal(a["sel"], b["sel"])
+    assert np.allclose(a["out"], b["out"], rtol=1e-4, atol=1e-6)
+    # and the storage is not an identity: unrotated storage of the same rows differs
+    c = o.sequence_kv8(dims, o.kv8_encode(Kr, False, 64.0), o.kv8_encode(Vr, False, 64.0), False,
+                       1 / 64.0, 1 / 64.0, kI, pos, q[pos], qI[pos], w[pos], gate[pos])
+    assert not np.allclose(c["out"], b["out"], rtol=1e-4, atol=1e-6)
+
+
 
 ALL_PINS = [pin_pool_exact, pin_pool_random, pin_scores_onehot, pin_scores_random,
             pin_value_gate, pin_topk_bruteforce, pin_worked_count, pin_width_bound,
             pin_token_set, pin_dense_equivalence, pin_sparse_vs_masked_sdpa,
             pin_zero_query_probe, pin_single_token, pin_gqa_equals_mha, pin_nan_poison,
-            pin_planted_selected]
+            pin_planted_selected, pin_e4m3_decode_matches_torch, pin_e4m3_encode_rounding,
+            pin_fwht_is_sylvester_hadamard, pin_kv8_storage_is_transparent_when_exact]

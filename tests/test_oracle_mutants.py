@@ -40,13 +40,29 @@ MUTANTS = {
                           "for (int64_t t = nb * r; t < n - 1; ++t) tokens[c++] = t;"),
     "tail_reads_future": ("int64_t n = p + 1, c = 0;", "int64_t n = p + 2, c = 0;"),
     "gqa_map_modulo": ("int32_t kvh = h / g;", "int32_t kvh = h % Hkv;"),
-    "gate_silu": ("double gt = 1.0 / (1.0 + exp(-(double)gate[(int64_t)h * D + x]));",
-                  "double gt = (double)gate[(int64_t)h * D + x] / (1.0 + exp(-(double)gate[(int64_t)h * D + x]));"),
+    "gate_silu": ("double gt = gate ? 1.0 / (1.0 + exp(-(double)gate[(int64_t)h * D + x])) : 1.0;",
+                  "double gt = gate ? (double)gate[(int64_t)h * D + x] / (1.0 + exp(-(double)gate[(int64_t)h * D + x])) : 1.0;"),
     "attn_no_scale": ("z[i] = scale * acc;", "z[i] = acc;"),
     "pv_reads_keys": ("const float* vr = V + (tokens[i] * Hkv + kvh) * D;",
                       "const float* vr = K + (tokens[i] * Hkv + kvh) * D;"),
     "dense_layer_drops_self": ("for (int64_t t = 0; t < n; ++t) tokens[c++] = t;",
                                "for (int64_t t = 0; t + 1 < n; ++t) tokens[c++] = t;"),
+    # 8-bit K/V storage and the rotated basis
+    "fwht_wrong_sign": ("x[j + len] = a - b;", "x[j + len] = b - a;"),
+    "e4m3_exponent_bias": ("ldexpf((float)(8 + m), e - 10)", "ldexpf((float)(8 + m), e - 9)"),
+    "e4m3_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "e4m3_no_saturation": ("if (a >= 448.0f) return sgn | 0x7E;",
+                           "if (a >= 480.0f) return sgn | 0x7F;"),
+    "kv8_encode_skips_rotation": ("if (rotate) qsa_oracle_fwht(t, D);",
+                                  "if (0) qsa_oracle_fwht(t, D);"),
+    "kv8_query_not_rotated": ("for (int64_t i = 0; i < nq * Hq; ++i) qsa_oracle_fwht(qr + i * D, D);",
+                              "for (int64_t i = 0; i < 0; ++i) qsa_oracle_fwht(qr + i * D, D);"),
+    "kv8_scores_not_divided": ("d2.attn_scale = (float)(a_scale / (double)D);",
+                               "d2.attn_scale = (float)a_scale;"),
+    "kv8_output_not_unrotated": ("        qsa_oracle_fwht(o, D);\n        for (int32_t x = 0; x < D; ++x) o[x] = o[x] / (float)D;",
+                                 "        for (int32_t x = 0; x < D; ++x) o[x] = o[x] / (float)D;"),
+    "kv8_v_scale_from_k": ("Vd[i] = qsa_oracle_e4m3_decode(Vc[i]) * v_scale;",
+                           "Vd[i] = qsa_oracle_e4m3_decode(Vc[i]) * k_scale;"),
 }
 
 
