@@ -100,6 +100,7 @@ def main():
     T = B * m
     Hq, Hkv, D, HI, dI = sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads, sp.idx_dim
     esz = 2  # bf16
+    kv_esz = 1 if sp.kv_fp8 else esz  # bytes per cached K/V element
 
     # Algorithmic bytes of one step (host formula from positions only): every
     # query reads its own selected (or, dense, all) K/V rows.
@@ -114,7 +115,7 @@ def main():
                     idx += nb * dI * 4              # pooled keys read by the scorer
                 else:
                     nsel = n
-                kv += nsel * Hkv * D * esz * 2
+                kv += nsel * Hkv * D * kv_esz * 2
         qgo = T * Hq * D * esz * 3 + (T * (HI * dI * esz + HI * 4) if r > 0 else 0)
         new_rows = T * (2 * Hkv * D + (dI if r > 0 else 0)) * esz
         return kv, idx, qgo + new_rows
@@ -198,12 +199,15 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": ("synthetic (seeded; " + (f"contexts U[{sp.ctx_lo},{sp.ctx_hi}]" if sp.ctx_hi
                                           else f"context {sp.ctx}") +
-                 "; N(0,1)/sqrt(d) q/k/v; decode inputs drawn on the GPU)"),
+                 "; N(0,1)/sqrt(d) q/k/v; decode inputs drawn on the GPU" +
+                 ("; K/V cached as E4M3 codes" + (" in the Hadamard basis" if sp.kv_rotate
+                                                  else "") if sp.kv_fp8 else "") + ")"),
         "config": {"workload": name, "batch": B, "q_per_step": m, "ctx_min": min(case.ctx),
                    "ctx_max": max(case.ctx), "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "block_size": r, "budget": sp.budget,
                    "idx_heads": HI, "idx_dim": dI, "paged": bool(sp.page_size),
-                   "layer_copies": L},
+                   "kv_cache": ("e4m3" + ("+hadamard" if sp.kv_rotate else "")) if sp.kv_fp8
+                   else "bf16", "layer_copies": L},
         "hbm_GBps_step": round(hbm_gbps, 1),
         "hbm_frac_step": round(hbm_gbps / HBM_PEAK_GBPS, 4),
         "step_bytes": {"selected_kv": kv0, "pooled_keys": idx0, "q_gate_out_new_rows": small0},
@@ -350,9 +354,28 @@ def cpu_baseline(case, sp, seconds):
 
     m = sp.q_per_step
 
+    codes = [None] * B
+    if sp.kv_fp8:  # the cache as the oracle stores it (outside the timed loop)
+        ks, vs = workloads.kv_scales(sp.head_dim, sp.kv_rotate)
+
+        def enc(b):
+            K, V, _ = f32[b]
+            inv_k = float(np.float32(1.0) / np.float32(ks))
+            inv_v = float(np.float32(1.0) / np.float32(vs))
+            codes[b] = (orc.kv8_encode(K, sp.kv_rotate, inv_k),
+                        orc.kv8_encode(V, sp.kv_rotate, inv_v))
+
+        with cf.ThreadPoolExecutor(max_workers=min(len(os.sched_getaffinity(0)), B)) as ex:
+            list(ex.map(enc, range(B)))
+
     def one(b):
         K, V, kI = f32[b]
         p = case.ctx[b]
+        if sp.kv_fp8:
+            orc.sequence_kv8(dims, codes[b][0], codes[b][1], sp.kv_rotate, ks, vs, kI,
+                             np.arange(p, p + m), case.q[b][:m], case.qI[b][:m],
+                             case.w[b][:m], case.gate[b][:m])
+            return
         orc.sequence(dims, K, V, kI, np.arange(p, p + m), case.q[b][:m], case.qI[b][:m],
                      case.w[b][:m], case.gate[b][:m])
 

@@ -82,6 +82,20 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   if (!(p.attn_scale == p.attn_scale) || !(p.idx_scale == p.idx_scale) || isinf(p.attn_scale) ||
       isinf(p.idx_scale))
     return fail(QSA_ERR_INVALID, "attn_scale / idx_scale must be finite");
+  if (p.kv_dtype != QSA_KV_SAME && p.kv_dtype != QSA_KV_FP8)
+    return fail(QSA_ERR_INVALID, "kv_dtype %d: QSA_KV_SAME (0) or QSA_KV_FP8 (2)", p.kv_dtype);
+  if (p.kv_rotate != 0 && p.kv_rotate != 1)
+    return fail(QSA_ERR_INVALID, "kv_rotate must be 0 or 1");
+  if (p.kv_dtype == QSA_KV_FP8) {
+    if (p.dtype != QSA_BF16 || p.head_dim != 128)
+      return fail(QSA_ERR_UNSUPPORTED, "QSA_KV_FP8 needs dtype QSA_BF16 and head_dim 128");
+    if (!(p.k_scale > 0.0f) || !(p.v_scale > 0.0f) || isinf(p.k_scale) || isinf(p.v_scale))
+      return fail(QSA_ERR_INVALID, "k_scale and v_scale must be finite and > 0");
+    if (p.kv_rotate && G < 4)
+      return fail(QSA_ERR_UNSUPPORTED, "kv_rotate needs n_q_heads/n_kv_heads >= 4");
+  } else if (p.kv_rotate) {
+    return fail(QSA_ERR_INVALID, "kv_rotate needs kv_dtype QSA_KV_FP8");
+  }
   if (b.n_seqs < 1) return fail(QSA_ERR_INVALID, "n_seqs (%d) must be >= 1", b.n_seqs);
   if (b.n_tokens < 0) return fail(QSA_ERR_INVALID, "n_tokens (%d) must be >= 0", b.n_tokens);
   if (b.n_tokens > 0) {
@@ -131,7 +145,16 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   g.pooled_ld = r ? (int32_t)round_up((b.kv_capacity + r - 1) / r, 64) : 0;
   g.nbcap = r ? b.max_kv_len / r : 0;
   const double a_scale = p.attn_scale > 0.0f ? (double)p.attn_scale : 1.0 / sqrt((double)g.D);
-  g.attn_scale_log2 = (float)(a_scale * 1.4426950408889634);
+  // 8-bit K/V: the K scale joins the softmax scale, and the rotated basis
+  // multiplies every score by D (H H = D I); the V scale and the 1/D of the
+  // un-rotation are applied to the output.
+  g.kv8 = p.kv_dtype == QSA_KV_FP8 ? 1 : 0;
+  g.rot = g.kv8 && p.kv_rotate ? 1 : 0;
+  g.inv_k_scale = g.kv8 ? 1.0f / p.k_scale : 1.0f;
+  g.inv_v_scale = g.kv8 ? 1.0f / p.v_scale : 1.0f;
+  g.out_scale = g.kv8 ? (float)((double)p.v_scale / (g.rot ? (double)g.D : 1.0)) : 1.0f;
+  g.attn_scale_log2 = (float)(a_scale * 1.4426950408889634 * (g.kv8 ? (double)p.k_scale : 1.0) /
+                              (g.rot ? (double)g.D : 1.0));
   g.idx_scale = r ? (p.idx_scale > 0.0f ? p.idx_scale : (float)(1.0 / sqrt((double)g.dI))) : 0.0f;
   g.inv_r = r ? 1.0f / (float)r : 0.0f;
   g.cu_q = b.cu_q;
@@ -154,7 +177,8 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   pl.attn.tiles = (int32_t)tiles;
   // Many (token, KV head) units, as in prefill: the MFMA kernel, one wave per
   // unit.  Few units (decode): the split-list bandwidth kernels.
-  pl.attn.mfma = (pl.elem == qsa::kBF16 && g.D == 128 && units >= kMfmaMinUnits) ? 1 : 0;
+  pl.attn.mfma =
+      (pl.elem == qsa::kBF16 && g.D == 128 && !g.kv8 && units >= kMfmaMinUnits) ? 1 : 0;
   if (pl.attn.mfma) pl.attn.n_splits = 1;
   splits = pl.attn.n_splits;
 
@@ -174,6 +198,7 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   // K/V cache rows are addressed by 32-bit row index inside the kernels.
   const int64_t kv_rows = b.page_size ? (int64_t)b.n_pages * g.Hkv * b.page_size
                                       : (int64_t)b.n_seqs * g.Hkv * b.kv_capacity;
+  g.kv_esz = g.kv8 ? 1 : (pl.elem == qsa::kBF16 ? 2 : 4);
   if (kv_rows > 0x7fffffff)
     return fail(QSA_ERR_UNSUPPORTED, "the K/V cache holds more than 2^31 rows");
   return QSA_OK;
@@ -223,6 +248,22 @@ size_t qsa_workspace_size(const qsa_params* params, const qsa_batch* batch) {
   Plan pl;
   if (resolve(params, batch, &pl) != QSA_OK) return 0;
   return pl.total;
+}
+
+qsa_status qsa_store_kv(const qsa_params* params, const qsa_batch* batch, const void* k_new,
+                        const void* v_new, void* k_cache, void* v_cache, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  QSA_TRY(resolve(params, batch, &pl));
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(need(k_new, "k_new", 16));
+  QSA_TRY(need(v_new, "v_new", 16));
+  QSA_TRY(need(k_cache, "k_cache", 16));
+  QSA_TRY(need(v_cache, "v_cache", 16));
+  return hip_status(qsa::launch_append_pool(pl.geo, pl.elem, k_new, v_new, nullptr, k_cache,
+                                            v_cache, nullptr, nullptr,
+                                            static_cast<hipStream_t>(stream)),
+                    "store launch");
 }
 
 qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,

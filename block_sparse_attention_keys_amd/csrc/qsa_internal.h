@@ -22,6 +22,11 @@ struct Geo {
   float attn_scale_log2;       // attn_scale * log2(e): softmax runs in base 2
   float idx_scale;             // indexer softmax scale (fp32, applied as c * d)
   float inv_r;                 // 1 / r, exact because r is a power of two
+  int32_t kv8;                 // 1: K/V caches hold OCP E4M3 codes (one byte per element)
+  int32_t rot;                 // 1: ... in the Sylvester-Hadamard-rotated basis
+  int32_t kv_esz;              // bytes per K/V cache element
+  float inv_k_scale, inv_v_scale;  // 8-bit: 1 / scale, the factor applied before encoding
+  float out_scale;             // 8-bit: V scale (and 1/D when rotated) on the attention output
   const int32_t* cu_q;
   const int32_t* past_len;
   const int32_t* page_table;

@@ -178,6 +178,90 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 }
 
 // ---------------------------------------------------------------------------
+// 8-bit K/V storage ("Porting Qwen4 to llama.cpp", section "Quantized KV Is
+// a Representation Contract").  OCP E4M3: 1 sign, 4 exponent bits (bias 7),
+// 3 mantissa bits, exponent 0 subnormal (m * 2^-9), no infinities, 448 the
+// largest finite value.  Encoding rounds to the nearest code, ties to the
+// even code, and saturates at +-448; NaN encodes as 0x7F.  The mantissa LSB
+// is the code's LSB, so rounding the scaled value to even is ties-to-even.
+__device__ __forceinline__ uint32_t e4m3_encode(float x) {
+  const uint32_t sgn = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a < 448.0f)) return (a != a) ? 0x7Fu : (sgn | 0x7Eu);
+  if (a < 0.015625f) return sgn | (uint32_t)__builtin_rintf(a * 512.0f);  // m * 2^-9, m <= 8
+  const int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;           // -6 .. 8
+  const int m = (int)__builtin_rintf(__builtin_ldexpf(a, 3 - e));           // 8 .. 16
+  return sgn | (uint32_t)((e + 7) * 8 + m - 8);  // m = 16 carries into the exponent
+}
+
+// Walsh-Hadamard butterfly stage across lanes for elements spread over
+// lanes: the partner element sits `dl` lanes away; the element whose index
+// has the stage bit set takes (partner - own), the other (own + partner), as
+// in the in-place transform (x[j], x[j+len]) <- (x[j] + x[j+len], x[j] - x[j+len]).
+__device__ __forceinline__ float fwht_cross(float v, int dl, bool upper) {
+  const float o = __shfl_xor(v, dl, 64);
+  return upper ? (o - v) : (v + o);
+}
+
+// One token's K and V rows (bf16 [Hkv][D], D = 128) into 8-bit caches, one
+// wave: lane l holds elements 2l, 2l+1 of a row; rotated (Sylvester Hadamard,
+// the standard butterfly order), scaled by 1/scale, encoded.  dst(kvh) is the
+// element offset of the row in the cache (one byte per element).
+template <typename RowOf>
+__device__ __forceinline__ void store_rows_kv8(const Geo& g, const uint16_t* __restrict__ k_src,
+                                               const uint16_t* __restrict__ v_src,
+                                               uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                               RowOf dst) {
+  const int lane = threadIdx.x & 63;
+  for (int rw = 0; rw < 2 * g.Hkv; ++rw) {
+    const int which = rw >= g.Hkv ? 1 : 0, kvh = rw - which * g.Hkv;
+    const uint16_t* src = (which ? v_src : k_src) + (int64_t)kvh * 128;
+    const uint32_t pr = *reinterpret_cast<const uint32_t*>(src + 2 * lane);
+    float x0 = __uint_as_float(pr << 16), x1 = __uint_as_float(pr & 0xFFFF0000u);
+    if (g.rot) {
+      const float a = x0, b = x1;
+      x0 = a + b;
+      x1 = a - b;
+#pragma unroll
+      for (int dl = 1; dl < 64; dl <<= 1) {
+        const bool up = (lane & dl) != 0;
+        x0 = fwht_cross(x0, dl, up);
+        x1 = fwht_cross(x1, dl, up);
+      }
+    }
+    const float inv = which ? g.inv_v_scale : g.inv_k_scale;
+    const uint32_t c = e4m3_encode(x0 * inv) | (e4m3_encode(x1 * inv) << 8);
+    const int64_t d = dst(kvh);
+    if (d >= 0) *reinterpret_cast<uint16_t*>((which ? vc : kc) + d + 2 * lane) = (uint16_t)c;
+  }
+}
+
+// The attention output of one head (D = 128) spread EPT consecutive dims per
+// thread over 128/EPT consecutive lanes of a wave (t_in: the thread's rank
+// among them): with the rotated basis, o = H o' (the 1/D is in out_scale),
+// then the 8-bit storage's output scale.  All lanes of the wave take part.
+template <int EPT>
+__device__ __forceinline__ void kv8_output(const Geo& g, float (&o)[EPT], int t_in) {
+  if (g.rot) {
+#pragma unroll
+    for (int len = 1; len < EPT; len <<= 1)
+#pragma unroll
+      for (int i = 0; i < EPT; ++i)
+        if (!(i & len)) {
+          const float a = o[i], b = o[i + len];
+          o[i] = a + b;
+          o[i + len] = a - b;
+        }
+#pragma unroll
+    for (int dl = 1; dl * EPT < 128; dl <<= 1)
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) o[i] = fwht_cross(o[i], dl, (t_in & dl) != 0);
+  }
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) o[i] *= g.out_scale;
+}
+
+// ---------------------------------------------------------------------------
 // append + pool: one workgroup per new token.
 template <typename E>
 __global__ __launch_bounds__(256) void append_pool_kernel(
@@ -188,7 +272,15 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
   const QueryPos qp = query_pos(g, t);
   if (!qp.ok) return;
   constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
-  if (k_new != nullptr) {
+  if (k_new != nullptr && g.kv8) {
+    if constexpr (sizeof(E) == 2) {
+      if (tid < 64)
+        store_rows_kv8(g, reinterpret_cast<const uint16_t*>(k_new) + (int64_t)t * g.Hkv * 128,
+                       reinterpret_cast<const uint16_t*>(v_new) + (int64_t)t * g.Hkv * 128,
+                       reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
+                       [&](int kvh) { return kv_row(g, qp.b, kvh, qp.p); });
+    }
+  } else if (k_new != nullptr) {
     const int units = g.D / EPV;
     const int per = g.Hkv * units;
     for (int u = tid; u < 2 * per; u += blockDim.x) {
@@ -322,7 +414,14 @@ __global__ __launch_bounds__(64) void score_kernel(
         *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * DI + min(lane, DI / EPV - 1) * EPV);
     const QueryPos qp = query_pos(g, t);
     if (!qp.ok) return;
-    for (int u = lane; u < kv_units; u += 64) {
+    if (g.kv8) {  // 8-bit storage: rotated, scaled and encoded rows
+      if constexpr (sizeof(E) == 2)
+        store_rows_kv8(g, reinterpret_cast<const uint16_t*>(k_new) + (int64_t)t * g.Hkv * 128,
+                       reinterpret_cast<const uint16_t*>(v_new) + (int64_t)t * g.Hkv * 128,
+                       reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
+                       [&](int kvh) { return kv_row(g, qp.b, kvh, qp.p); });
+    }
+    for (int u = lane; u < (g.kv8 ? 0 : kv_units); u += 64) {
       const int which = u >= per ? 1 : 0, rem = u - which * per;
       const int kvh = rem / units, c = rem - kvh * units;
       const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
@@ -885,9 +984,14 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(Geo g, AttnPlan plan,
   if (flag < 0.0f) return;
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
 #pragma unroll
+  for (int i = 0; i < EPT; ++i) O[i] *= inv;
+  if constexpr (D == 128) {
+    if (g.kv8) kv8_output(g, O, d0 / EPT);
+  }
+#pragma unroll
   for (int i = 0; i < EPT; ++i) {
     const float sg = 1.0f / (1.0f + expf(-gt[i]));
-    out[ob + i] = from_f32<E>(O[i] * inv * sg);
+    out[ob + i] = from_f32<E>(O[i] * sg);
   }
 }
 
@@ -1078,7 +1182,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 // SEL: the top-k selection is made here from the scores (each workgroup of a
 // token makes the same selection; the workgroup of split 0, KV head 0 stores
 // it in sel / nblk when they are given), instead of being read from sel.
-template <int G, bool BUF, bool SEL>
+template <int G, bool BUF, bool SEL, bool KV8>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     Geo g, AttnPlan plan, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
@@ -1116,9 +1220,39 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   // Step 1 of the row resolution (independent loads).
   {
     const int hq = tid >> 4, ch = tid & 15;
-    qs[hq][ch] = hq < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0 + hq) * D +
-                                                          8 * ch)
-                        : make_uint4(0u, 0u, 0u, 0u);
+    uint4 qv = hq < G ? *reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0 + hq) * D +
+                                                        8 * ch)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    if constexpr (KV8) {
+      if (g.rot) {
+        // K/V are stored rotated: the query joins them (q' = H q).  16 lanes
+        // hold a head, 8 dimensions each: three stages in the lane, four
+        // across lanes; rounded back to bf16.
+        const uint32_t w4[4] = {qv.x, qv.y, qv.z, qv.w};
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = __uint_as_float(w4[i] << 16);
+          x[2 * i + 1] = __uint_as_float(w4[i] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (!(i & len)) {
+              const float a = x[i], b = x[i + len];
+              x[i] = a + b;
+              x[i + len] = a - b;
+            }
+#pragma unroll
+        for (int dl = 1; dl < 16; dl <<= 1)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = fwht_cross(x[i], dl, (ch & dl) != 0);
+        qv = make_uint4(bf16_rne(x[0]) | (bf16_rne(x[1]) << 16), bf16_rne(x[2]) | (bf16_rne(x[3]) << 16),
+                        bf16_rne(x[4]) | (bf16_rne(x[5]) << 16), bf16_rne(x[6]) | (bf16_rne(x[7]) << 16));
+      }
+    }
+    qs[hq][ch] = qv;
   }
   int nk_raw = 0;
   int32_t sv[EPR], pg[EPR];
@@ -1262,6 +1396,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const int r1 = min(r0 + RR, i1);
     uint4 kr[4][4];          // [token group][dim step]: A operands
     uint2 vr[32];            // tokens 32*half + j, dims 4*c32 .. +3
+    // 8-bit storage: a lane's 32 contiguous bytes of a K row (dims 32*q4 ..
+    // +31; the MFMA k-slots are permuted to match, the query too), and 4
+    // bytes of a V row (dims 4*c32 .. +3) per token.
+    uint4 k8[4][2];
+    uint32_t v8[32];
     uint32_t vmask = 0u;     // without BUF: bit j set = V row of token 32*half + j valid
     // at < 0: no tile.
     auto load_k = [&](int at) {
@@ -1270,7 +1409,21 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const int32_t rj = rr[16 * gi + c16] | none;
-        if constexpr (BUF) {
+        if constexpr (KV8) {
+          if constexpr (BUF) {
+            const uint32_t off = rj >= 0 ? (uint32_t)rj * D + 32u * q4 : kOobOffset;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              k8[gi][hh] = __builtin_bit_cast(
+                  uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, off, 16 * hh, kStreamPolicy));
+          } else {
+            const uint8_t* src = reinterpret_cast<const uint8_t*>(kc) + (int64_t)max(rj, 0) * D + 32 * q4;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              k8[gi][hh] = __builtin_bit_cast(
+                  uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + 16 * hh)));
+          }
+        } else if constexpr (BUF) {
           const uint32_t off = rj >= 0 ? (uint32_t)rj * (D * 2) + 16u * q4 : kOobOffset;
 #pragma unroll
           for (int db = 0; db < 4; ++db)
@@ -1292,7 +1445,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         const int32_t rj = rr[j] | none;
-        if constexpr (BUF) {
+        if constexpr (KV8) {
+          if constexpr (BUF) {
+            const uint32_t off = rj >= 0 ? (uint32_t)rj * D + 4u * c32 : kOobOffset;
+            v8[j] = __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, kStreamPolicy);
+          } else {
+            v8[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
+                reinterpret_cast<const uint8_t*>(vc) + (int64_t)max(rj, 0) * D + 4 * c32));
+            vm |= (rj >= 0 ? 1u : 0u) << j;
+          }
+        } else if constexpr (BUF) {
           const uint32_t off = rj >= 0 ? (uint32_t)rj * (D * 2) + 8u * c32 : kOobOffset;
           vr[j] = __builtin_bit_cast(
               uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamPolicy));
@@ -1316,16 +1478,29 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
         uint4 qb[4];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) qb[db] = qs[c16][4 * db + q4];
+        for (int db = 0; db < 4; ++db) qb[db] = qs[c16][KV8 ? 4 * q4 + db : 4 * db + q4];
         f32x4_t z[4];
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) {
           z[gi] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int db = 0; db < 4; ++db)
+          for (int db = 0; db < 4; ++db) {
+            uint4 a;
+            if constexpr (KV8) {  // 8 codes -> 8 bf16 (exact)
+              const uint4 h = k8[gi][db >> 1];
+              const uint32_t w0 = (db & 1) ? h.z : h.x, w1 = (db & 1) ? h.w : h.y;
+              a = make_uint4(
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true)));
+            } else {
+              a = kr[gi][db];
+            }
             z[gi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, kr[gi][db]), __builtin_bit_cast(bf16x8_t, qb[db]),
-                z[gi], 0, 0, 0);
+                __builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, qb[db]), z[gi], 0,
+                0, 0);
+          }
         }
 
         // Lane holds head c16 for tokens 16*gi + 4*q4 + e.
@@ -1370,8 +1545,24 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int tp = 0; tp < 16; ++tp) {
-          uint2 va = vr[2 * tp], vb = vr[2 * tp + 1];
-          if constexpr (!BUF) {
+          uint2 va, vb;
+          if constexpr (KV8) {  // 4 codes -> 4 bf16 (exact), masked rows zeroed first
+            uint32_t a8 = v8[2 * tp], b8 = v8[2 * tp + 1];
+            if constexpr (!BUF) {
+              a8 &= ((vmask >> (2 * tp)) & 1u) ? ~0u : 0u;
+              b8 &= ((vmask >> (2 * tp + 1)) & 1u) ? ~0u : 0u;
+            }
+            va = make_uint2(
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a8, 1.0f, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a8, 1.0f, true)));
+            vb = make_uint2(
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b8, 1.0f, false)),
+                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b8, 1.0f, true)));
+          } else {
+            va = vr[2 * tp];
+            vb = vr[2 * tp + 1];
+          }
+          if constexpr (!BUF && !KV8) {
             const uint32_t ka = ((vmask >> (2 * tp)) & 1u) ? ~0u : 0u;
             const uint32_t kb = ((vmask >> (2 * tp + 1)) & 1u) ? ~0u : 0u;
             va.x &= ka;
@@ -1441,13 +1632,18 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 
   if (plan.n_splits == 1) {
-    if (!ok || !has_elem) return;
+    if (!ok) return;
     const float inv = Lw > 0.0f ? 1.0f / Lw : 0.0f;
+    float Of[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) Of[i] = Ow[i] * inv;
+    if constexpr (KV8) kv8_output(g, Of, d0 / EPT);
+    if (!has_elem) return;
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
       const int64_t idx = ((int64_t)t * g.Hq + h0 + hh) * D + d0 + i;
       const float sg = 1.0f / (1.0f + expf(-to_f32(gate[idx])));
-      out[idx] = from_f32<uint16_t>(Ow[i] * inv * sg);
+      out[idx] = from_f32<uint16_t>(Of[i] * sg);
     }
     return;
   }
@@ -1688,9 +1884,9 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
   if constexpr (sizeof(E) == 2 && D == 128) {
     const int64_t rows = g.page_table ? (int64_t)g.n_pages * g.Hkv * g.page_size
                                       : (int64_t)g.B * g.Hkv * g.cap;
-    const int64_t bytes = rows * D * 2;
-    auto launch = [&](auto buf, auto fused) {
-      attn_decode_kernel<G, decltype(buf)::value, decltype(fused)::value>
+    const int64_t bytes = rows * D * g.kv_esz;
+    auto launch = [&](auto buf, auto fused, auto kv8) {
+      attn_decode_kernel<G, decltype(buf)::value, decltype(fused)::value, decltype(kv8)::value>
           <<<grid, 64 * kWaves, 0, st>>>(
               g, plan, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
               static_cast<const uint16_t*>(v_cache), sel, n_blocks,
@@ -1698,13 +1894,17 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
               decltype(buf)::value ? (uint32_t)bytes : 0u, scores, sel_out, nblk_out);
     };
     const bool buf = bytes < (int64_t)kOobOffset;
-    if (scores != nullptr) {
-      if (buf) launch(std::true_type{}, std::true_type{});
-      else launch(std::false_type{}, std::true_type{});
-    } else {
-      if (buf) launch(std::true_type{}, std::false_type{});
-      else launch(std::false_type{}, std::false_type{});
-    }
+    auto launch_kv = [&](auto kv8) {
+      if (scores != nullptr) {
+        if (buf) launch(std::true_type{}, std::true_type{}, kv8);
+        else launch(std::false_type{}, std::true_type{}, kv8);
+      } else {
+        if (buf) launch(std::true_type{}, std::false_type{}, kv8);
+        else launch(std::false_type{}, std::false_type{}, kv8);
+      }
+    };
+    if (g.kv8) launch_kv(std::true_type{});
+    else launch_kv(std::false_type{});
   } else {
     attn_split_kernel<E, G, D><<<grid, 64, 0, st>>>(
         g, plan, static_cast<const E*>(q), static_cast<const E*>(k_cache),

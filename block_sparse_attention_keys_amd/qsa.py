@@ -22,16 +22,19 @@ QSA_ERR_WORKSPACE = -3
 QSA_ERR_HIP = -4
 QSA_F32 = 0
 QSA_BF16 = 1
+QSA_KV_SAME = 0
+QSA_KV_FP8 = 2
 
 EXPORTS = ["qsa_last_error", "qsa_pooled_ld", "qsa_workspace_size", "qsa_pool_keys",
-           "qsa_score_select", "qsa_attend", "qsa_forward"]
+           "qsa_store_kv", "qsa_score_select", "qsa_attend", "qsa_forward"]
 
 
 class qsa_params(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("n_idx_heads", C.c_int32), ("idx_dim", C.c_int32), ("block_size", C.c_int32),
                 ("ratio", C.c_int32), ("budget", C.c_int32), ("attn_scale", C.c_float),
-                ("idx_scale", C.c_float), ("dtype", C.c_int32)]
+                ("idx_scale", C.c_float), ("dtype", C.c_int32), ("kv_dtype", C.c_int32),
+                ("kv_rotate", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
 
 
 class qsa_batch(C.Structure):
@@ -69,6 +72,8 @@ def lib(path: str = LIB_PATH) -> C.CDLL:
     L.qsa_workspace_size.argtypes = [P, B]
     L.qsa_pool_keys.restype = C.c_int
     L.qsa_pool_keys.argtypes = [P, B, vp, vp, vp, vp]
+    L.qsa_store_kv.restype = C.c_int
+    L.qsa_store_kv.argtypes = [P, B, vp, vp, vp, vp, vp]
     L.qsa_score_select.restype = C.c_int
     L.qsa_score_select.argtypes = [P, B, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
     L.qsa_attend.restype = C.c_int
@@ -112,10 +117,11 @@ def last_error() -> str:
 
 
 def make_params(n_q_heads, n_kv_heads, head_dim, n_idx_heads, idx_dim, block_size, budget,
-                dtype, ratio=None, attn_scale=0.0, idx_scale=0.0) -> qsa_params:
+                dtype, ratio=None, attn_scale=0.0, idx_scale=0.0, kv_dtype=QSA_KV_SAME,
+                kv_rotate=0, k_scale=1.0, v_scale=1.0) -> qsa_params:
     return qsa_params(n_q_heads, n_kv_heads, head_dim, n_idx_heads, idx_dim, block_size,
                       block_size if ratio is None else ratio, budget, attn_scale, idx_scale,
-                      dtype)
+                      dtype, kv_dtype, kv_rotate, k_scale, v_scale)
 
 
 class Batch:
@@ -143,6 +149,11 @@ def qsa_workspace_size(params: qsa_params, batch) -> int:
 def qsa_pool_keys(params, batch, k_idx_new, k_idx_cache, pooled, stream=None) -> None:
     _check(lib().qsa_pool_keys(C.byref(params), C.byref(_b(batch)), _ptr(k_idx_new),
                                _ptr(k_idx_cache), _ptr(pooled), _stream(stream)))
+
+
+def qsa_store_kv(params, batch, k_new, v_new, k_cache, v_cache, stream=None) -> None:
+    _check(lib().qsa_store_kv(C.byref(params), C.byref(_b(batch)), _ptr(k_new), _ptr(v_new),
+                              _ptr(k_cache), _ptr(v_cache), _stream(stream)))
 
 
 def qsa_score_select(params, batch, q_idx, w, pooled, sel, n_blocks, scores=None, ws=None,

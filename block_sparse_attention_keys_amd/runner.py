@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import qsa
-from .workloads import BF16, Case
+from .workloads import BF16, Case, kv_scales
 
 
 def _dev(a: np.ndarray, device, dtype: str) -> torch.Tensor:
@@ -39,7 +39,9 @@ class DeviceCase:
     def __init__(self, case: Case, device="cuda", n_layers: int = 1, extra_steps: int = 0,
                  layout: Optional[str] = None, attn_scale: float = 0.0,
                  idx_scale: float = 0.0, budget: Optional[int] = None,
-                 block_size: Optional[int] = None, page_offset: int = 0):
+                 block_size: Optional[int] = None, page_offset: int = 0,
+                 kv_fp8: Optional[bool] = None, kv_rotate: Optional[bool] = None,
+                 kv_scale: Optional[tuple] = None):
         sp = case.spec
         self.case, self.spec, self.device = case, sp, torch.device(device)
         self.dt = torch.bfloat16 if sp.dtype == BF16 else torch.float32
@@ -47,10 +49,20 @@ class DeviceCase:
         self.B = B
         r = sp.block_size if block_size is None else block_size
         self.r = r
+        self.kv8 = sp.kv_fp8 if kv_fp8 is None else kv_fp8
+        self.kv_rotate = bool(self.kv8 and (sp.kv_rotate if kv_rotate is None else kv_rotate))
+        if not self.kv8:
+            kv_scale = (1.0, 1.0)
+        elif kv_scale is None:
+            kv_scale = kv_scales(sp.head_dim, self.kv_rotate)
+        self.k_scale, self.v_scale = (float(x) for x in kv_scale)
         self.params = qsa.make_params(sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads,
                                       sp.idx_dim, r, sp.budget if budget is None else budget,
                                       qsa.QSA_BF16 if sp.dtype == BF16 else qsa.QSA_F32,
-                                      attn_scale=attn_scale, idx_scale=idx_scale)
+                                      attn_scale=attn_scale, idx_scale=idx_scale,
+                                      kv_dtype=qsa.QSA_KV_FP8 if self.kv8 else qsa.QSA_KV_SAME,
+                                      kv_rotate=int(self.kv_rotate), k_scale=self.k_scale,
+                                      v_scale=self.v_scale)
         self.n_tok = [int(x.shape[0]) for x in case.k]
         cap_tok = max(self.n_tok) + extra_steps
         self.paged = (layout or ("paged" if sp.page_size else "contiguous")) == "paged"
@@ -101,8 +113,9 @@ class DeviceCase:
     # ------------------------------------------------------------------ setup
     def _alloc(self, kv_shape, ki_shape) -> dict:
         sp = self.spec
-        st = {"k": torch.zeros(kv_shape, dtype=self.dt, device=self.device),
-              "v": torch.zeros(kv_shape, dtype=self.dt, device=self.device)}
+        kv_dt = torch.uint8 if self.kv8 else self.dt
+        st = {"k": torch.zeros(kv_shape, dtype=kv_dt, device=self.device),
+              "v": torch.zeros(kv_shape, dtype=kv_dt, device=self.device)}
         if self.r > 0:
             st["kI"] = torch.zeros(ki_shape, dtype=self.dt, device=self.device)
             b0 = self.batch_for([0] * self.B, [1] * self.B)
@@ -112,6 +125,15 @@ class DeviceCase:
                                        device=self.device)
         return st
 
+    def cached_rows(self, which: str, b: int, n: int, layer: int = 0) -> torch.Tensor:
+        """Rows [0, n) of sequence b of cache `which` ("k" or "v") as [n][Hkv][D]."""
+        st = self.layers[layer][which]
+        s = torch.arange(n, device=self.device)
+        if self.paged:
+            pg, off = self._rows(b, s)
+            return st[pg, :, off, :]
+        return st[b, :, :n, :].permute(1, 0, 2)
+
     def _rows(self, b: int, s: torch.Tensor):
         """Cache coordinates of token positions s of sequence b."""
         if self.paged:
@@ -120,8 +142,9 @@ class DeviceCase:
         return None, s
 
     def _fill_context(self, st: dict) -> None:
-        """Copy each sequence's cached context rows into the caches, then pool
-        the context's indexer keys with the library kernel."""
+        """Copy each sequence's cached context rows into the caches (8-bit
+        caches: stored by the library's qsa_store_kv, one sequence at a
+        time), then pool the context's indexer keys with the library kernel."""
         case = self.case
         ctx = case.ctx
         for b in range(self.B):
@@ -131,7 +154,13 @@ class DeviceCase:
             s = torch.arange(n, device=self.device)
             kk = _dev(case.k[b][:n], self.device, self.spec.dtype)
             vv = _dev(case.v[b][:n], self.device, self.spec.dtype)
-            if self.paged:
+            if self.kv8:
+                counts = [0] * self.B
+                counts[b] = n
+                qsa.qsa_store_kv(self.params, self.batch_for([0] * self.B, counts), kk, vv,
+                                 st["k"], st["v"])
+                torch.cuda.synchronize(self.device)
+            elif self.paged:
                 pg, off = self._rows(b, s)
                 st["k"][pg, :, off, :] = kk
                 st["v"][pg, :, off, :] = vv

@@ -70,10 +70,24 @@ class Spec:
     planted: int = 0                  # number of planted blocks per sequence
     planted_spread: bool = False      # True: block ids 8 + 16 i; else random
     planted_density: float = 0.0      # fraction of candidate blocks (overrides planted)
+    # K/V cache storage: 8-bit E4M3 codes with per-tensor scales, optionally
+    # in the Hadamard-rotated basis (False: the compute dtype)
+    kv_fp8: bool = False
+    kv_rotate: bool = False
 
     @property
     def k_blocks(self) -> int:
         return self.budget // self.block_size if self.block_size > 0 else 0
+
+
+def kv_scales(head_dim: int, rotate: bool) -> tuple:
+    """Per-tensor scales (k_scale, v_scale) of an 8-bit K/V cache for the
+    draws below (K, V ~ N(0, 1/D); the rotated values H x ~ N(0, 1)): eight
+    standard deviations of the stored values map to E4M3's largest finite
+    value 448, so no draw saturates in practice."""
+    sd = 1.0 if rotate else head_dim ** -0.5
+    s = float(np.float32(8.0 * sd / 448.0))
+    return s, s
 
 
 SPECS: Dict[str, Spec] = {
@@ -110,6 +124,13 @@ SPECS: Dict[str, Spec] = {
         n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,
         block_size=64, budget=4096, ctx_lo=8192, ctx_hi=131072, steps=1,
         q_per_step=4, page_size=64),
+    # The ragged decode with the K/V cache stored as 8-bit E4M3 codes in the
+    # Hadamard-rotated basis (the quantized-KV storage contract).
+    "ragged_paged_decode_128k_fp8kv": Spec(
+        name="ragged_paged_decode_128k_fp8kv", kind="decode", dtype=BF16, n_seqs=32,
+        n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,
+        block_size=64, budget=4096, ctx_lo=8192, ctx_hi=131072, steps=1,
+        page_size=64, kv_fp8=True, kv_rotate=True),
     "mtp_dense_ragged_bf16": Spec(
         name="mtp_dense_ragged_bf16", kind="decode", dtype=BF16, n_seqs=32,
         n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,

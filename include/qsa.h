@@ -44,6 +44,7 @@
  *      w                    [T][H_I]                      fp32
  *      k_cache, v_cache     contiguous: [B][Hkv][kv_capacity][D]
  *                           paged:      [n_pages][Hkv][page_size][D]
+ *                           (elements of params.kv_dtype)
  *      k_idx_cache          contiguous: [B][kv_capacity][d_I]
  *                           paged:      [n_pages][page_size][d_I]
  *      pooled               [B][d_I][pooled_ld]   fp32, column-major per
@@ -75,6 +76,22 @@ typedef enum {
 
 typedef enum { QSA_F32 = 0, QSA_BF16 = 1 } qsa_dtype;
 
+/* Storage of the K/V caches ("Porting Qwen4 to llama.cpp", section "Quantized
+ * KV Is a Representation Contract": quantized K/V may live in a
+ * Hadamard-rotated basis, and a QSA attention path must honour that storage).
+ *  QSA_KV_SAME: elements of params.dtype.
+ *  QSA_KV_FP8:  one byte per element, OCP E4M3 (1 sign, 4 exponent bits with
+ *               bias 7, 3 mantissa bits, no infinities, largest finite 448);
+ *               a stored code c of K stands for e4m3(c) * k_scale, of V for
+ *               e4m3(c) * v_scale.  With kv_rotate = 1 every stored row is
+ *               H x, H the Sylvester Hadamard matrix of order D (entries
+ *               +-1); the attention rotates the query and un-rotates its
+ *               output (H o' / D), so results are those of the plain basis.
+ *               The library encodes rows it appends: x (rotated if asked)
+ *               times the fp32 value 1.0f / scale, rounded to the nearest code
+ *               (ties to even), saturating at +-448. */
+typedef enum { QSA_KV_SAME = 0, QSA_KV_FP8 = 2 } qsa_kv_dtype;
+
 /* Layer geometry (host values). */
 typedef struct {
   int32_t n_q_heads;   /* Hq, a multiple of n_kv_heads */
@@ -89,6 +106,12 @@ typedef struct {
   float attn_scale;    /* <= 0 selects D^-0.5 */
   float idx_scale;     /* <= 0 selects d_I^-0.5 */
   int32_t dtype;       /* qsa_dtype of q, k, v, gate, out, q_idx, k_idx */
+  int32_t kv_dtype;    /* qsa_kv_dtype of k_cache / v_cache; QSA_KV_FP8 needs dtype
+                          QSA_BF16 and D = 128 */
+  int32_t kv_rotate;   /* QSA_KV_FP8 only: 1 = rows stored in the rotated basis
+                          (needs Hq/Hkv >= 4) */
+  float k_scale;       /* QSA_KV_FP8: scale of the K codes (> 0) */
+  float v_scale;       /* QSA_KV_FP8: scale of the V codes (> 0) */
 } qsa_params;
 
 /* One call's batch (host sizes for launch geometry + device metadata). */
@@ -128,6 +151,13 @@ size_t qsa_workspace_size(const qsa_params* params, const qsa_batch* batch);
  * in fp32.  Only new blocks are touched, O(new tokens) -- not the whole-cache
  * recompute of the upstream reference ("The trap the layer loop walks into").
  * Dense layer (block_size 0): QSA_ERR_INVALID. */
+/* K/V append only: writes k_new[t], v_new[t] to rows past_len[b] + (t -
+ * cu_q[b]) of k_cache / v_cache under the layer's storage (QSA_KV_FP8: rotated
+ * if asked, scaled and encoded as above).  For filling a cache with context
+ * rows; qsa_forward appends its own new rows. */
+qsa_status qsa_store_kv(const qsa_params* params, const qsa_batch* batch, const void* k_new,
+                        const void* v_new, void* k_cache, void* v_cache, void* stream);
+
 qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,
                          const void* k_idx_new, void* k_idx_cache, float* pooled,
                          void* stream);

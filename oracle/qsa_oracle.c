@@ -298,23 +298,28 @@ float qsa_oracle_e4m3_decode(uint8_t c) {
   return sgn ? -v : v;
 }
 
-/* Nearest finite code by direct search over the 127 non-negative codes
- * (their values increase with the code); ties go to the even code. */
+/* Nearest finite code.  The 127 non-negative finite codes have values that
+ * increase with the code, so bisection finds the first code whose value is
+ * >= |x|; the nearer of it and the code below it wins, ties to the even
+ * code. */
 uint8_t qsa_oracle_e4m3_encode(float x) {
   if (isnan(x)) return 0x7F;
   const uint8_t sgn = signbit(x) ? 0x80 : 0x00;
   const float a = fabsf(x);
   if (a >= 448.0f) return sgn | 0x7E;
-  int best = 0;
-  double best_d = INFINITY;
-  for (int c = 0; c <= 0x7E; ++c) {
-    const double d = fabs((double)qsa_oracle_e4m3_decode((uint8_t)c) - (double)a);
-    if (d < best_d || (d == best_d && (c & 1) == 0)) {
-      best = c;
-      best_d = d;
-    }
+  int lo = 0, hi = 0x7E; /* decode(hi) >= a throughout */
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    if (qsa_oracle_e4m3_decode((uint8_t)mid) >= a) hi = mid;
+    else lo = mid + 1;
   }
-  return sgn | (uint8_t)best;
+  int c = hi;
+  if (c > 0) {
+    const double up = (double)qsa_oracle_e4m3_decode((uint8_t)c) - (double)a;
+    const double dn = (double)a - (double)qsa_oracle_e4m3_decode((uint8_t)(c - 1));
+    if (dn < up || (dn == up && ((c - 1) & 1) == 0)) c = c - 1;
+  }
+  return sgn | (uint8_t)c;
 }
 
 /* In-place Walsh-Hadamard transform of x[0..n), n a power of two: H_n x with

@@ -45,6 +45,19 @@ class SeqF32:
                              workloads.as_f32(c.kI[b]))
         return self.cache[b]
 
+    def codes(self, b, dc, orc=None):
+        """The oracle's 8-bit storage codes of sequence b's K and V under
+        dc's storage (rotation, scales)."""
+        key = ("codes", b, dc.kv_rotate, dc.k_scale, dc.v_scale)
+        if key not in self.cache:
+            orc = orc or oracle.load()
+            K, V, _ = self.get(b)
+            inv_k = float(np.float32(1.0) / np.float32(dc.k_scale))
+            inv_v = float(np.float32(1.0) / np.float32(dc.v_scale))
+            self.cache[key] = (orc.kv8_encode(K, dc.kv_rotate, inv_k),
+                               orc.kv8_encode(V, dc.kv_rotate, inv_v))
+        return self.cache[key]
+
 
 def run_calls(dc: runner.DeviceCase, calls: Optional[List[int]] = None, keep=None):
     """Run calls in order; return per kept call (out, sel, n_blocks, spans)."""
@@ -83,8 +96,15 @@ def check_call(dc, seqf: SeqF32, result, sample: Optional[int] = None, rng_seed:
         K, V, kI = seqf.get(b)
         qbase = int(case.q_pos[b][0])
         qi = (s - qbase) + idx
-        ref = orc.sequence(dims, K, V, kI, s + idx, case.q[b][qi], case.qI[b][qi],
-                           case.w[b][qi], case.gate[b][qi], want_scores=dims["block_size"] > 0)
+        if getattr(dc, "kv8", False):
+            Kc, Vc = seqf.codes(b, dc, orc)
+            ref = orc.sequence_kv8(dims, Kc, Vc, dc.kv_rotate, dc.k_scale, dc.v_scale, kI,
+                                   s + idx, case.q[b][qi], case.qI[b][qi], case.w[b][qi],
+                                   case.gate[b][qi], want_scores=dims["block_size"] > 0)
+        else:
+            ref = orc.sequence(dims, K, V, kI, s + idx, case.q[b][qi], case.qI[b][qi],
+                               case.w[b][qi], case.gate[b][qi],
+                               want_scores=dims["block_size"] > 0)
         got = out[t0 + idx]
         ok, st = parity.outputs_ok(got, ref["out"], dtype)
         assert ok, f"seq {b} outputs {st}"

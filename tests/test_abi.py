@@ -88,6 +88,15 @@ def fwd(L, p, b, ptr=FAKE, ws_bytes=1 << 30):
     (dict(idx_dim=48), qsa.QSA_ERR_UNSUPPORTED, "idx_dim"),
     (dict(dtype=7), qsa.QSA_ERR_INVALID, "dtype"),
     (dict(attn_scale=float("nan")), qsa.QSA_ERR_INVALID, "finite"),
+    (dict(kv_dtype=1), qsa.QSA_ERR_INVALID, "kv_dtype"),
+    (dict(kv_dtype=qsa.QSA_KV_FP8, kv_rotate=2), qsa.QSA_ERR_INVALID, "kv_rotate"),
+    (dict(kv_rotate=1), qsa.QSA_ERR_INVALID, "needs kv_dtype"),
+    (dict(kv_dtype=qsa.QSA_KV_FP8, dtype=qsa.QSA_F32), qsa.QSA_ERR_UNSUPPORTED, "QSA_KV_FP8"),
+    (dict(kv_dtype=qsa.QSA_KV_FP8, head_dim=64), qsa.QSA_ERR_UNSUPPORTED, "QSA_KV_FP8"),
+    (dict(kv_dtype=qsa.QSA_KV_FP8, k_scale=0.0), qsa.QSA_ERR_INVALID, "k_scale"),
+    (dict(kv_dtype=qsa.QSA_KV_FP8, v_scale=float("inf")), qsa.QSA_ERR_INVALID, "k_scale"),
+    (dict(kv_dtype=qsa.QSA_KV_FP8, kv_rotate=1, n_q_heads=4), qsa.QSA_ERR_UNSUPPORTED,
+     "kv_rotate"),
 ])
 def test_params_rejected(L, kw, status, needle):
     assert fwd(L, P(**kw), Bt()) == status
@@ -135,6 +144,17 @@ def test_zero_tokens_is_a_noop(L):
     assert qsa.qsa_workspace_size(P(), b) == 0
     assert fwd(L, P(), b, ptr=None, ws_bytes=0) == qsa.QSA_OK
     assert L.qsa_attend(C.byref(P()), C.byref(b), *([None] * 8), 0, None) == qsa.QSA_OK
+
+
+def test_store_kv_validates(L):
+    p = P(kv_dtype=qsa.QSA_KV_FP8)
+    assert L.qsa_store_kv(C.byref(p), C.byref(Bt()), FAKE, None, FAKE, FAKE, None) == \
+        qsa.QSA_ERR_INVALID
+    assert "v_new" in qsa.last_error()
+    assert L.qsa_store_kv(C.byref(P(kv_rotate=1)), C.byref(Bt()), FAKE, FAKE, FAKE, FAKE,
+                          None) == qsa.QSA_ERR_INVALID
+    b = Bt(n_tokens=0, cu_q=None, past_len=None)
+    assert L.qsa_store_kv(C.byref(p), C.byref(b), None, None, None, None, None) == qsa.QSA_OK
 
 
 def test_dense_layer_rejects_indexer_calls(L):

@@ -50,7 +50,7 @@ MUTANTS = {
     # 8-bit K/V storage and the rotated basis
     "fwht_wrong_sign": ("x[j + len] = a - b;", "x[j + len] = b - a;"),
     "e4m3_exponent_bias": ("ldexpf((float)(8 + m), e - 10)", "ldexpf((float)(8 + m), e - 9)"),
-    "e4m3_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "e4m3_ties_to_odd": ("(dn == up && ((c - 1) & 1) == 0)", "(dn == up && ((c - 1) & 1) == 1)"),
     "e4m3_no_saturation": ("if (a >= 448.0f) return sgn | 0x7E;",
                            "if (a >= 480.0f) return sgn | 0x7F;"),
     "kv8_encode_skips_rotation": ("if (rotate) qsa_oracle_fwht(t, D);",
