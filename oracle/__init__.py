@@ -21,7 +21,8 @@ DEFAULT_LIB = os.path.join(HERE, "libqsa_oracle.so")
 class Dims(C.Structure):
     _fields_ = [("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
                 ("n_idx_heads", C.c_int32), ("idx_dim", C.c_int32), ("block_size", C.c_int32),
-                ("budget", C.c_int32), ("attn_scale", C.c_float), ("idx_scale", C.c_float)]
+                ("budget", C.c_int32), ("attn_scale", C.c_float), ("idx_scale", C.c_float),
+                ("idx_rope_dim", C.c_int32), ("idx_rope_theta", C.c_float)]
 
 
 def _f32(a) -> np.ndarray:
@@ -69,6 +70,9 @@ class Oracle:
             C.POINTER(C.c_float), C.POINTER(C.c_int32), C.POINTER(C.c_int32),
             C.POINTER(C.c_int64), C.POINTER(C.c_float), C.c_int64]
 
+        L.qsa_oracle_rope_rows.restype = None
+        L.qsa_oracle_rope_rows.argtypes = [C.POINTER(C.c_float), C.c_int64, C.c_int32, C.c_int32,
+                                           C.c_double, C.POINTER(C.c_int64)]
         L.qsa_oracle_e4m3_decode.restype = C.c_float
         L.qsa_oracle_e4m3_decode.argtypes = [C.c_uint8]
         L.qsa_oracle_e4m3_encode.restype = C.c_uint8
@@ -88,6 +92,19 @@ class Oracle:
 
     def threads(self) -> int:
         return int(self._L.qsa_oracle_threads())
+
+    # --- rotary position embedding ---------------------------------------------
+    def rope(self, x, R: int, theta: float, pos) -> np.ndarray:
+        """qsa_oracle_rope on every row of x [..., n]; pos broadcasts against
+        x.shape[:-1] (one position per row)."""
+        x = np.array(_f32(x), np.float32, copy=True)
+        n = x.shape[-1]
+        P = np.ascontiguousarray(np.broadcast_to(np.asarray(pos, np.int64), x.shape[:-1]).reshape(-1))
+        flat = x.reshape(-1, n)
+        if flat.shape[0]:
+            self._L.qsa_oracle_rope_rows(_p(flat), flat.shape[0], n, int(R), float(theta),
+                                         _p(P, C.c_int64))
+        return x
 
     # --- 8-bit K/V storage ----------------------------------------------------
     def e4m3_decode(self, codes) -> np.ndarray:

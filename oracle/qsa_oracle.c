@@ -52,6 +52,8 @@ typedef struct {
   int32_t budget;      /* tokens; k = budget / r complete blocks */
   float attn_scale;    /* <= 0: 1/sqrt(D) */
   float idx_scale;     /* <= 0: 1/sqrt(d_I) */
+  int32_t idx_rope_dim;  /* > 0: rotary dims of each pooled key (see qsa_oracle_rope) */
+  float idx_rope_theta;  /* base of those rotary frequencies */
 } qsa_oracle_dims;
 
 int qsa_oracle_threads(void) {
@@ -77,6 +79,35 @@ int64_t qsa_oracle_pool(const float* kI, int64_t n_tok, int32_t d_idx, int32_t r
     }
   }
   return nb;
+}
+
+/* Rotary position embedding in the rotate-half form on the first R entries
+ * of x (R even; the entries from R on are left alone), at position pos with
+ * base theta.  For i < R/2 the pair (x[i], x[i + R/2]) turns by the angle
+ * pos * f_i with f_i = theta^(-2i/R):
+ *   x'[i] = x[i]*c - x[i+R/2]*s,   x'[i+R/2] = x[i+R/2]*c + x[i]*s.
+ * f_i = pow(theta, -2i/R) and the angle are fp64, c and s are the fp64
+ * cosine and sine rounded to fp32, and the rotation is fp32 (each product
+ * rounded, then the sum).  (LocalAI QSA-block commit, opening paragraph:
+ * the block applies RoPE after the q/k norms; fresh-review section: the
+ * indexer query and the pooled indexer keys are rotated with the same
+ * angles.) */
+void qsa_oracle_rope(float* x, int32_t R, double theta, int64_t pos) {
+  const int32_t h = R / 2;
+  for (int32_t i = 0; i < h; ++i) {
+    const double f = pow(theta, -2.0 * (double)i / (double)R);
+    const double ang = (double)pos * f;
+    const float c = (float)cos(ang), sn = (float)sin(ang);
+    const float a = x[i], b = x[i + h];
+    x[i] = a * c - b * sn;
+    x[i + h] = b * c + a * sn;
+  }
+}
+
+/* qsa_oracle_rope on `rows` rows of n entries, row i at position pos[i]. */
+void qsa_oracle_rope_rows(float* x, int64_t rows, int32_t n, int32_t R, double theta,
+                          const int64_t* pos) {
+  for (int64_t i = 0; i < rows; ++i) qsa_oracle_rope(x + i * n, R, theta, pos[i]);
 }
 
 /* Relu-weighted multi-head block score (DeepSeek-style indexer logits with
@@ -227,6 +258,7 @@ int qsa_oracle_sequence(const qsa_oracle_dims* dm, int64_t n_tok, const float* K
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv || D <= 0 || r < 0) return -1;
   const int32_t k = r > 0 ? dm->budget / r : 0;
   if (r > 0 && (k < 1 || HI <= 0 || dI <= 0)) return -1;
+  if (dm->idx_rope_dim < 0 || dm->idx_rope_dim % 2 || dm->idx_rope_dim > dI) return -1;
   for (int64_t i = 0; i < nq; ++i)
     if (pos[i] < 0 || pos[i] >= n_tok) return -1;
   const double a_scale = dm->attn_scale > 0.0f ? (double)dm->attn_scale
@@ -236,7 +268,13 @@ int qsa_oracle_sequence(const qsa_oracle_dims* dm, int64_t n_tok, const float* K
   float* pooled = NULL;
   if (r > 0) {
     pooled = (float*)malloc(sizeof(float) * (size_t)((n_tok / r) * dI + 1));
-    qsa_oracle_pool(kI, n_tok, dI, r, pooled);
+    const int64_t nbt = qsa_oracle_pool(kI, n_tok, dI, r, pooled);
+    /* With rotary indexer keys, the pooled key of block j is rotated at the
+     * block's first position j*r (the pages do not state the position; the
+     * block start is the reading taken). */
+    if (dm->idx_rope_dim > 0)
+      for (int64_t j = 0; j < nbt; ++j)
+        qsa_oracle_rope(pooled + j * dI, dm->idx_rope_dim, (double)dm->idx_rope_theta, j * r);
   }
   int rc = 0;
 #pragma omp parallel for schedule(dynamic, 1)

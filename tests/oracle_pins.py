@@ -462,9 +462,216 @@ def pin_kv8_storage_is_transparent_when_exact(o):
 
 
 
+# ------------------------------------------------------------- block front end
+def _complex_rope(x, R, theta, pos):
+    """Rotate-half RoPE written as complex multiplication in float64: the
+    pair (x_i, x_{i+R/2}) is the complex number x_i + j x_{i+R/2}, turned by
+    exp(j pos theta^(-2i/R))."""
+    x = np.asarray(x, np.float64).copy()
+    h = R // 2
+    if h == 0:
+        return x
+    i = np.arange(h, dtype=np.float64)
+    ang = np.asarray(pos, np.float64)[..., None] * np.power(float(theta), -2.0 * i / R)
+    z = (x[..., :h] + 1j * x[..., h:R]) * np.exp(1j * ang)
+    x[..., :h], x[..., h:R] = z.real, z.imag
+    return x
+
+
+def pin_rope_against_complex_rotation(o):
+    """RoPE equals the complex-number rotation of each rotate-half pair; at
+    position 0 it is the identity bit for bit; values past the rotary dims
+    are untouched bit for bit."""
+    rng = np.random.default_rng(40)
+    for n, R, theta in ((16, 16, 10000.0), (64, 32, 1e6), (12, 8, 500.0)):
+        x = rng.standard_normal((7, n)).astype(np.float32)
+        pos = np.array([0, 1, 2, 17, 1000, 65535, 262143])
+        got = o.rope(x, R, theta, pos)
+        ref = _complex_rope(x, R, theta, pos)
+        assert np.abs(got - ref).max() < 4 * EPS32 * np.abs(x).max() * 2, (n, R)
+        assert np.array_equal(got[0], x[0])
+        assert np.array_equal(got[:, R:], x[:, R:])
+
+
+def pin_rope_relative_position(o):
+    """<rope(q, p), rope(k, s)> depends on p - s only (shift both by m)."""
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((5, 32)).astype(np.float32)
+    k = rng.standard_normal((5, 32)).astype(np.float32)
+    p, s = np.array([3, 50, 700, 9, 1]), np.array([0, 49, 100, 9, 300])
+    for m in (1, 37, 4096):
+        a = np.sum(o.rope(q, 32, 10000.0, p).astype(np.float64) *
+                   o.rope(k, 32, 10000.0, s), axis=1)
+        b = np.sum(o.rope(q, 32, 10000.0, p + m).astype(np.float64) *
+                   o.rope(k, 32, 10000.0, s + m), axis=1)
+        assert np.abs(a - b).max() < 1e-4, m
+
+
+def pin_rms_norm_closed_forms(o):
+    """RMSNorm with the (1 + w) weight: a constant row c gives
+    sign(c) (1 + w) / sqrt(1 + eps/c^2); a row with mean square 1 and eps 0
+    gives x (1 + w); the result does not change when the row is scaled."""
+    from oracle import block as ob
+    w = np.linspace(-0.5, 0.5, 8).astype(np.float32)
+    for c in (2.0, -0.25):
+        got = ob.rms_norm(np.full((1, 8), c, np.float32), w, 1e-6)
+        ref = np.sign(c) * (1.0 + w.astype(np.float64)) / math.sqrt(1.0 + 1e-6 / c ** 2)
+        assert np.abs(got[0] - ref).max() < 2 * EPS32
+    x = np.array([[1, -1, 1, 1, -1, -1, 1, -1]], np.float32)
+    assert np.array_equal(ob.rms_norm(x, w, 0.0), (x * (1.0 + w)).astype(np.float32))
+    y = np.random.default_rng(42).standard_normal((3, 8)).astype(np.float32)
+    assert np.abs(ob.rms_norm(y, w, 0.0) - ob.rms_norm(4 * y, w, 0.0)).max() < 4 * EPS32
+
+
+def pin_pooled_key_rotation(o):
+    """With rotary indexer keys each pooled key is rotated at its block's
+    first position: scores equal the float64 formula on means rotated by
+    complex multiplication at j*r."""
+    rng = np.random.default_rng(43)
+    Hq, Hkv, D, HI, dI, r, n = 2, 1, 8, 2, 16, 4, 37
+    K, V, kI, q, qI, w, gate = _rand_seq(rng, n, Hq, Hkv, D, HI, dI)
+    dims = _dims(Hq, Hkv, D, HI, dI, r, 8)
+    dims.update(idx_rope_dim=12, idx_rope_theta=100.0)
+    pos = np.array([n - 1, 20])
+    res = o.sequence(dims, K, V, kI, pos, q[pos], qI[pos], w[pos], gate[pos], want_scores=True)
+    nb = n // r
+    pooled = kI[:nb * r].astype(np.float64).reshape(nb, r, dI).mean(axis=1)
+    pooled = _complex_rope(pooled, 12, 100.0, np.arange(nb) * r)
+    c = 1.0 / math.sqrt(dI)
+    for t, p in enumerate(pos):
+        nbt = (p + 1) // r
+        ref = (w[p][:, None] * np.maximum(c * qI[p].astype(np.float64) @ pooled[:nbt].T, 0)).sum(0)
+        assert np.abs(res["scores"][t, :nbt] - ref).max() < 1e-5 * max(1.0, np.abs(ref).max())
+
+
+def _block_dims(**kw):
+    bd = dict(n_q_heads=4, n_kv_heads=2, head_dim=16, n_idx_heads=2, idx_dim=8, block_size=4,
+              budget=8, attn_scale=0.0, idx_scale=0.0, idx_rope_dim=8, idx_rope_theta=1000.0,
+              rotary_dim=8, rope_theta=10000.0, norm_eps=1e-6)
+    bd.update(kw)
+    return bd
+
+
+def pin_block_reduces_to_core(o):
+    """Stacked identity projections, rows of mean square 1 with eps 0 and
+    zero norm weights, no rotation, o_proj = [I; 0]: the block is the core
+    QSA on the slices of x, and y its attention output."""
+    from oracle import block as ob
+    rng = np.random.default_rng(44)
+    bd = _block_dims(rotary_dim=0, idx_rope_dim=0, norm_eps=0.0)
+    Hq, Hkv, D, HI, dI = 4, 2, 16, 2, 8
+    rows = ob.split_rows(bd)
+    dm = rows["total"]
+    n = 23
+    x = (rng.standard_normal((n, dm)) * 0.5).astype(np.float32)
+    a, b = rows["q"]
+    x[:, a:b] = np.where(rng.random((n, b - a)) < 0.5, -1.0, 1.0)
+    a, b = rows["k"]
+    x[:, a:b] = np.where(rng.random((n, b - a)) < 0.5, -1.0, 1.0)
+    x = ob.bf16_round(x)
+    Wo = np.zeros((dm, Hq * D), np.float32)
+    Wo[:Hq * D] = np.eye(Hq * D, dtype=np.float32)
+    pos = np.array([n - 1, 13, 5])
+    res = ob.block(o, bd, x, np.eye(dm, dtype=np.float32), np.zeros(D, np.float32),
+                   np.zeros(D, np.float32), Wo, pos)
+    sl = lambda name, shape: x[:, slice(*rows[name])].reshape(n, *shape)  # noqa: E731
+    ref = o.sequence(ob.core_dims(bd), sl("k", (Hkv, D)), sl("v", (Hkv, D)), sl("kI", (dI,)),
+                     pos, sl("q", (Hq, D))[pos], sl("qI", (HI, dI))[pos],
+                     np.ones((3, HI), np.float32), sl("gate", (Hq, D))[pos])
+    assert np.array_equal(res["sel"], ref["sel"])
+    assert np.array_equal(res["y"][:, :Hq * D], ob.bf16_round(ref["out"]).reshape(3, -1))
+    assert not res["y"][:, Hq * D:].any()
+
+
+def _torch_block(bd, x, W_in, qn, kn, W_o):
+    """The dense QSA block (budget >= context) from torch library routines in
+    float64: linear, rms_norm, complex-number RoPE, scaled_dot_product_attention
+    (causal, GQA by repetition), sigmoid gate, linear; rounded to bf16 where
+    the path stores bf16 (torch's own bfloat16 conversion)."""
+    F = torch.nn.functional
+    T = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
+    bf = lambda t: t.to(torch.bfloat16).to(torch.float64)  # noqa: E731
+    Hq, Hkv, D = bd["n_q_heads"], bd["n_kv_heads"], bd["head_dim"]
+    n = x.shape[0]
+    P = F.linear(T(x), T(W_in)).to(torch.float32).to(torch.float64)
+    o = 0
+    def take(m):
+        nonlocal o
+        t = P[:, o:o + m]
+        o += m
+        return t
+    q, g, k, v = take(Hq * D), take(Hq * D), take(Hkv * D), take(Hkv * D)
+    q = F.rms_norm(q.reshape(n, Hq, D), (D,), eps=bd["norm_eps"]) * (1 + T(qn))
+    k = F.rms_norm(k.reshape(n, Hkv, D), (D,), eps=bd["norm_eps"]) * (1 + T(kn))
+    pos = np.arange(n)[:, None]
+    q = bf(T(_complex_rope(q.numpy(), bd["rotary_dim"], bd["rope_theta"], pos)))
+    k = bf(T(_complex_rope(k.numpy(), bd["rotary_dim"], bd["rope_theta"], pos)))
+    v, g = bf(v.reshape(n, Hkv, D)), bf(g.reshape(n, Hq, D))
+    rep = Hq // Hkv
+    att = F.scaled_dot_product_attention(
+        q.permute(1, 0, 2)[None], k.permute(1, 0, 2).repeat_interleave(rep, 0)[None].contiguous(),
+        v.permute(1, 0, 2).repeat_interleave(rep, 0)[None].contiguous(), is_causal=True)
+    att = att[0].permute(1, 0, 2) * torch.sigmoid(g)
+    return F.linear(bf(att.reshape(n, Hq * D)), T(W_o)).numpy()
+
+
+def pin_block_dense_matches_torch(o):
+    """Budget above the context (every block selected) and the dense layer:
+    the oracle's block equals the block built from torch routines."""
+    from oracle import block as ob
+    rng = np.random.default_rng(45)
+    n, dm = 29, 24
+    for r, budget in ((4, 64), (0, 0)):
+        bd = _block_dims(block_size=r, budget=budget)
+        if r == 0:
+            bd.update(n_idx_heads=0, idx_dim=0, idx_rope_dim=0)
+        rows = ob.split_rows(bd)
+        x = ob.bf16_round(rng.standard_normal((n, dm)).astype(np.float32))
+        W_in = ob.bf16_round((rng.standard_normal((rows["total"], dm)) / math.sqrt(dm)).astype(np.float32))
+        qn = ob.bf16_round((0.3 * rng.standard_normal(16)).astype(np.float32))
+        kn = ob.bf16_round((0.3 * rng.standard_normal(16)).astype(np.float32))
+        W_o = ob.bf16_round((rng.standard_normal((dm, 64)) / 8).astype(np.float32))
+        got = ob.block(o, bd, x, W_in, qn, kn, W_o, np.arange(n))["y"]
+        ref = _torch_block(bd, x, W_in, qn, kn, W_o)
+        err = np.abs(got - ref).max()
+        assert err < 2e-4 * np.abs(ref).max(), (r, err)
+
+
+def pin_block_index_scores(o):
+    """The block's pre-top-k scores above the budget equal the indexer built
+    from float64 numpy: rotated indexer query at the token's position, raw
+    indexer keys mean-pooled, each mean rotated at its block's first
+    position (complex-number RoPE), relu-weighted with all-ones weights."""
+    from oracle import block as ob
+    rng = np.random.default_rng(46)
+    n, dm = 41, 24
+    bd = _block_dims(block_size=4, budget=8)
+    rows = ob.split_rows(bd)
+    x = ob.bf16_round(rng.standard_normal((n, dm)).astype(np.float32))
+    W_in = ob.bf16_round((rng.standard_normal((rows["total"], dm)) / math.sqrt(dm)).astype(np.float32))
+    z16 = np.zeros(16, np.float32)
+    W_o = np.zeros((dm, 64), np.float32)
+    pos = np.array([n - 1, 30, 17])
+    res = ob.block(o, bd, x, W_in, z16, z16, W_o, pos, want_scores=True)
+    P = x.astype(np.float64) @ W_in.astype(np.float64).T
+    qI = P[:, slice(*rows["qI"])].reshape(n, 2, 8)
+    kI = ob.bf16_round(P[:, slice(*rows["kI"])].astype(np.float32)).astype(np.float64)
+    nb = n // 4
+    pooled = _complex_rope(kI[:nb * 4].reshape(nb, 4, 8).mean(axis=1), 8, 1000.0,
+                           np.arange(nb) * 4)
+    for t, p in enumerate(pos):
+        qr = _complex_rope(qI[p], 8, 1000.0, np.full(2, p))
+        nbt = (p + 1) // 4
+        ref = np.maximum(qr @ pooled[:nbt].T / math.sqrt(8), 0).sum(0)
+        assert np.abs(res["scores"][t, :nbt] - ref).max() < 5e-3 * np.abs(ref).max(), p
+
+
 ALL_PINS = [pin_pool_exact, pin_pool_random, pin_scores_onehot, pin_scores_random,
             pin_value_gate, pin_topk_bruteforce, pin_worked_count, pin_width_bound,
             pin_token_set, pin_dense_equivalence, pin_sparse_vs_masked_sdpa,
             pin_zero_query_probe, pin_single_token, pin_gqa_equals_mha, pin_nan_poison,
             pin_planted_selected, pin_e4m3_decode_matches_torch, pin_e4m3_encode_rounding,
-            pin_fwht_is_sylvester_hadamard, pin_kv8_storage_is_transparent_when_exact]
+            pin_fwht_is_sylvester_hadamard, pin_kv8_storage_is_transparent_when_exact,
+            pin_rope_against_complex_rotation, pin_rope_relative_position,
+            pin_rms_norm_closed_forms, pin_pooled_key_rotation, pin_block_reduces_to_core,
+            pin_block_dense_matches_torch, pin_block_index_scores]

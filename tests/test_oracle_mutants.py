@@ -63,12 +63,42 @@ MUTANTS = {
                                  "        for (int32_t x = 0; x < D; ++x) o[x] = o[x] / (float)D;"),
     "kv8_v_scale_from_k": ("Vd[i] = qsa_oracle_e4m3_decode(Vc[i]) * v_scale;",
                            "Vd[i] = qsa_oracle_e4m3_decode(Vc[i]) * k_scale;"),
+    "rope_sign": ("x[i] = a * c - b * sn;", "x[i] = a * c + b * sn;"),
+    "rope_second_half_sign": ("x[i + h] = b * c + a * sn;", "x[i + h] = b * c - a * sn;"),
+    "rope_frequency_exponent": ("pow(theta, -2.0 * (double)i / (double)R)",
+                                "pow(theta, -1.0 * (double)i / (double)R)"),
+    "rope_adjacent_pairs": ("const float a = x[i], b = x[i + h];",
+                            "const float a = x[i], b = x[i ^ 1];"),
+    "pooled_rope_block_index": ("(double)dm->idx_rope_theta, j * r);",
+                                "(double)dm->idx_rope_theta, j);"),
+    "pooled_rope_skipped": ("if (dm->idx_rope_dim > 0)\n", "if (dm->idx_rope_dim > 100000)\n"),
+}
+
+# Mistakes planted in the block front end (oracle/block.py), one at a time.
+PY_SRC = os.path.join(ROOT, "oracle", "block.py")
+PY_MUTANTS = {
+    "norm_weight_polarity": ("* (1.0 + widen(w).astype(np.float64))",
+                             "* (widen(w).astype(np.float64))"),
+    "norm_sum_not_mean": ("ms = np.mean(x64 * x64, axis=-1, keepdims=True)",
+                          "ms = np.sum(x64 * x64, axis=-1, keepdims=True)"),
+    "gate_rows_before_q": ('sizes = [("q", Hq * D), ("gate", Hq * D),',
+                           'sizes = [("gate", Hq * D), ("q", Hq * D),'),
+    "query_rope_next_position": ('t = orc.rope(t, bd["rotary_dim"], bd["rope_theta"], pos[:, None])',
+                                 't = orc.rope(t, bd["rotary_dim"], bd["rope_theta"], pos[:, None] + 1)'),
+    "index_query_not_rotated": ('t = orc.rope(P.reshape(n, HI, dI), bd["idx_rope_dim"],',
+                                't = orc.rope(P.reshape(n, HI, dI), 0,'),
+    "k_norm_uses_q_weight": ('qn_w if name == "q" else kn_w', 'qn_w'),
+    "o_proj_of_unrounded": ('ref["y"] = project(attn, W_o)', 'ref["y"] = project(attn * 1.01, W_o)'),
 }
 
 
 def test_every_mutant_is_distinct_and_applies():
     text = open(SRC).read()
     for name, (a, b) in MUTANTS.items():
+        assert text.count(a) == 1, name
+        assert a != b, name
+    text = open(PY_SRC).read()
+    for name, (a, b) in PY_MUTANTS.items():
         assert text.count(a) == 1, name
         assert a != b, name
 
@@ -101,4 +131,41 @@ def test_mutant_is_killed(name, tmp_path):
     env["OMP_NUM_THREADS"] = "2"
     proc = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
                           text=True, timeout=300)
+    assert proc.returncode != 0, f"mutant {name} survived every pin"
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_block_mutant_is_killed(name, tmp_path):
+    """A copy of the oracle package with one mistake in block.py, loaded
+    first on the path of a child process, against the unmodified C oracle."""
+    import shutil
+    a, b = PY_MUTANTS[name]
+    text = open(PY_SRC).read()
+    assert text.count(a) == 1
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    for f in ("__init__.py", "build.py"):
+        shutil.copy(os.path.join(ROOT, "oracle", f), pkg / f)
+    (pkg / "block.py").write_text(text.replace(a, b))
+    lib = os.path.join(ROOT, "oracle", "libqsa_oracle.so")
+    if not os.path.exists(lib):
+        ob.build(lib)
+    code = (
+        "import sys, oracle, oracle_pins\n"
+        "assert oracle.__file__.startswith(%r)\n"
+        f"m = oracle.load({lib!r})\n"
+        "failed = []\n"
+        "for pin in oracle_pins.ALL_PINS:\n"
+        "    try:\n"
+        "        pin(m)\n"
+        "    except (AssertionError, ValueError):\n"
+        "        failed.append(pin.__name__)\n"
+        "print('FAILED_PINS', failed)\n"
+        "sys.exit(1 if failed else 0)\n") % str(tmp_path)
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([str(tmp_path), ROOT, HERE, env.get("PYTHONPATH", "")])
+    env["OMP_NUM_THREADS"] = "2"
+    proc = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True,
+                          text=True, timeout=300, cwd=str(tmp_path))
+    assert "FAILED_PINS" in proc.stdout, proc.stderr[-2000:]
     assert proc.returncode != 0, f"mutant {name} survived every pin"
