@@ -96,6 +96,14 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   } else if (p.kv_rotate) {
     return fail(QSA_ERR_INVALID, "kv_rotate needs kv_dtype QSA_KV_FP8");
   }
+  if (p.idx_rope_dim != 0) {
+    if (r == 0) return fail(QSA_ERR_INVALID, "idx_rope_dim must be 0 for a dense layer");
+    if (p.idx_rope_dim < 0 || p.idx_rope_dim % 2 || p.idx_rope_dim > p.idx_dim)
+      return fail(QSA_ERR_INVALID, "idx_rope_dim %d: an even number in [0, idx_dim]",
+                  p.idx_rope_dim);
+    if (!(p.idx_rope_theta > 0.0f) || isinf(p.idx_rope_theta))
+      return fail(QSA_ERR_INVALID, "idx_rope_theta must be finite and > 0");
+  }
   if (b.n_seqs < 1) return fail(QSA_ERR_INVALID, "n_seqs (%d) must be >= 1", b.n_seqs);
   if (b.n_tokens < 0) return fail(QSA_ERR_INVALID, "n_tokens (%d) must be >= 0", b.n_tokens);
   if (b.n_tokens > 0) {
@@ -148,6 +156,11 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   // 8-bit K/V: the K scale joins the softmax scale, and the rotated basis
   // multiplies every score by D (H H = D I); the V scale and the 1/D of the
   // un-rotation are applied to the output.
+  g.idx_rope_dim = p.idx_rope_dim;
+  for (int i = 0; i < 64; ++i)
+    g.idx_freq[i] = i < p.idx_rope_dim / 2
+                        ? pow((double)p.idx_rope_theta, -2.0 * (double)i / (double)p.idx_rope_dim)
+                        : 0.0;
   g.kv8 = p.kv_dtype == QSA_KV_FP8 ? 1 : 0;
   g.rot = g.kv8 && p.kv_rotate ? 1 : 0;
   g.inv_k_scale = g.kv8 ? 1.0f / p.k_scale : 1.0f;
@@ -231,6 +244,13 @@ qsa_status hip_status(hipError_t e, const char* what) {
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+qsa_status forward_launch(const Plan& pl, const qsa_batch* batch, const void* q,
+                          const void* k_new, const void* v_new, const void* q_idx,
+                          const void* k_idx_new, const float* w, const void* gate,
+                          void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                          void* out, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
+                          hipStream_t st);
 
 }  // namespace
 
@@ -360,7 +380,23 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
     if (n_blocks_opt) QSA_TRY(need(n_blocks_opt, "n_blocks", 4));
   }
   QSA_TRY(check_ws(pl, ws, ws_bytes));
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  return forward_launch(pl, batch, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cache, v_cache,
+                        k_idx_cache, pooled, out, sel_opt, n_blocks_opt, ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of one QSA layer step (arguments already validated).
+qsa_status forward_launch(const Plan& pl, const qsa_batch* batch, const void* q,
+                          const void* k_new, const void* v_new, const void* q_idx,
+                          const void* k_idx_new, const float* w, const void* gate,
+                          void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                          void* out, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
+                          hipStream_t st) {
+  const bool qsa_layer = pl.geo.r != 0;
   int32_t* sel = sel_opt ? sel_opt : reinterpret_cast<int32_t*>(ws_at(ws, pl.off_sel));
   int32_t* nblk = n_blocks_opt ? n_blocks_opt : reinterpret_cast<int32_t*>(ws_at(ws, pl.off_nblk));
   if (qsa_layer && batch->max_q_len == 1) {
@@ -403,4 +439,145 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
                     "attend launch");
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// The block front end.
+namespace {
+
+struct BlockPlan {
+  Plan core;
+  int n_in, d_model, hqd, S1, S2;
+  size_t off_p1, off_q, off_gate, off_k, off_v, off_qI, off_kI, off_w, off_attn, off_p2,
+      off_core, total;
+};
+
+qsa_status resolve_block(const qsa_params* P, const qsa_block_params* BP, const qsa_batch* Bt,
+                         BlockPlan* out) {
+  QSA_TRY(resolve(P, Bt, &out->core));
+  if (BP == nullptr) return fail(QSA_ERR_INVALID, "block params are NULL");
+  const qsa_params& p = *P;
+  const qsa_block_params& bp = *BP;
+  if (p.dtype != QSA_BF16) return fail(QSA_ERR_UNSUPPORTED, "the block needs dtype QSA_BF16");
+  if (bp.d_model <= 0 || bp.d_model % 32 != 0 || bp.d_model > 65536)
+    return fail(QSA_ERR_INVALID, "d_model %d: a positive multiple of 32, at most 65536",
+                bp.d_model);
+  if (bp.rotary_dim < 0 || bp.rotary_dim % 2 || bp.rotary_dim > p.head_dim)
+    return fail(QSA_ERR_INVALID, "rotary_dim %d: an even number in [0, head_dim]", bp.rotary_dim);
+  if (bp.rotary_dim > 0 && (!(bp.rope_theta > 0.0f) || isinf(bp.rope_theta)))
+    return fail(QSA_ERR_INVALID, "rope_theta must be finite and > 0");
+  if (!(bp.norm_eps >= 0.0f) || isinf(bp.norm_eps))
+    return fail(QSA_ERR_INVALID, "norm_eps must be finite and >= 0");
+  const qsa::Geo& g = out->core.geo;
+  const int64_t T = Bt->n_tokens;
+  const int64_t hqd = (int64_t)g.Hq * g.D, hkvd = (int64_t)g.Hkv * g.D;
+  const int64_t n_in = 2 * hqd + 2 * hkvd + (g.r ? (int64_t)g.HI * g.dI + g.dI : 0);
+  const int64_t lim = int64_t(1) << 31;  // operand bytes the GEMM addresses
+  if (T * bp.d_model * 2 >= lim || n_in * bp.d_model * 2 >= lim || hqd * bp.d_model * 2 >= lim ||
+      T * hqd * 2 >= lim)
+    return fail(QSA_ERR_UNSUPPORTED, "a projection operand reaches 2 GiB");
+  out->n_in = (int)n_in;
+  out->d_model = bp.d_model;
+  out->hqd = (int)hqd;
+  out->S1 = T > 0 ? qsa::gemm_splits((int)T, (int)n_in, bp.d_model) : 1;
+  out->S2 = T > 0 ? qsa::gemm_splits((int)T, bp.d_model, (int)hqd) : 1;
+  size_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const size_t o = off;
+    off += round_up(std::max<int64_t>(bytes, 1), kAlign);
+    return o;
+  };
+  out->off_p1 = take(out->S1 * T * n_in * 4);
+  out->off_q = take(T * hqd * 2);
+  out->off_gate = take(T * hqd * 2);
+  out->off_k = take(T * hkvd * 2);
+  out->off_v = take(T * hkvd * 2);
+  out->off_qI = take(T * g.HI * g.dI * 2);
+  out->off_kI = take(T * g.dI * 2);
+  out->off_w = take(T * g.HI * 4);
+  out->off_attn = take(T * hqd * 2);
+  out->off_p2 = take(out->S2 * T * bp.d_model * 4);
+  out->off_core = take((int64_t)out->core.total);
+  out->total = T > 0 ? off : 0;
+  return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qsa_block_workspace_size(const qsa_params* params, const qsa_block_params* block,
+                                const qsa_batch* batch) {
+  BlockPlan bl;
+  if (resolve_block(params, block, batch, &bl) != QSA_OK) return 0;
+  return bl.total;
+}
+
+qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* block,
+                             const qsa_batch* batch, const void* x, const void* w_in,
+                             const void* q_norm, const void* k_norm, const void* w_o,
+                             void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                             void* y, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
+                             size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  BlockPlan bl;
+  QSA_TRY(resolve_block(params, block, batch, &bl));
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(need(x, "x", 16));
+  QSA_TRY(need(w_in, "w_in", 16));
+  QSA_TRY(need(q_norm, "q_norm", 2));
+  QSA_TRY(need(k_norm, "k_norm", 2));
+  QSA_TRY(need(w_o, "w_o", 16));
+  QSA_TRY(need(k_cache, "k_cache", 16));
+  QSA_TRY(need(v_cache, "v_cache", 16));
+  QSA_TRY(need(y, "y", 16));
+  const qsa::Geo& g = bl.core.geo;
+  if (g.r != 0) {
+    QSA_TRY(need(k_idx_cache, "k_idx_cache", 16));
+    QSA_TRY(need(pooled, "pooled", 16));
+    if (sel_opt) QSA_TRY(need(sel_opt, "sel", 4));
+    if (n_blocks_opt) QSA_TRY(need(n_blocks_opt, "n_blocks", 4));
+  }
+  if (ws == nullptr || ws_bytes < bl.total)
+    return fail(QSA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed",
+                ws ? ws_bytes : (size_t)0, bl.total);
+  if (!aligned(ws, 16)) return fail(QSA_ERR_INVALID, "workspace must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int T = batch->n_tokens;
+  float* p1 = reinterpret_cast<float*>(ws_at(ws, bl.off_p1));
+  QSA_TRY(hip_status(qsa::launch_proj_gemm(x, w_in, p1, T, bl.n_in, bl.d_model, bl.S1, st),
+                     "input projection launch"));
+  qsa::BlockPrepArgs a;
+  a.part = p1;
+  a.S = bl.S1;
+  a.n_in = bl.n_in;
+  a.eps = block->norm_eps;
+  a.rotary_dim = block->rotary_dim;
+  for (int i = 0; i < 64; ++i)
+    a.freq[i] = i < block->rotary_dim / 2
+                    ? pow((double)block->rope_theta, -2.0 * (double)i / (double)block->rotary_dim)
+                    : 0.0;
+  a.q_norm = static_cast<const uint16_t*>(q_norm);
+  a.k_norm = static_cast<const uint16_t*>(k_norm);
+  a.q = reinterpret_cast<uint16_t*>(ws_at(ws, bl.off_q));
+  a.gate = reinterpret_cast<uint16_t*>(ws_at(ws, bl.off_gate));
+  a.k = reinterpret_cast<uint16_t*>(ws_at(ws, bl.off_k));
+  a.v = reinterpret_cast<uint16_t*>(ws_at(ws, bl.off_v));
+  a.q_idx = reinterpret_cast<uint16_t*>(ws_at(ws, bl.off_qI));
+  a.k_idx = reinterpret_cast<uint16_t*>(ws_at(ws, bl.off_kI));
+  a.w = reinterpret_cast<float*>(ws_at(ws, bl.off_w));
+  QSA_TRY(hip_status(qsa::launch_block_prep(g, a, st), "block prep launch"));
+  void* attn = ws_at(ws, bl.off_attn);
+  QSA_TRY(forward_launch(bl.core, batch, a.q, a.k, a.v, g.r ? a.q_idx : nullptr,
+                         g.r ? a.k_idx : nullptr, g.r ? a.w : nullptr, a.gate, k_cache, v_cache,
+                         k_idx_cache, pooled, attn, sel_opt, n_blocks_opt,
+                         ws_at(ws, bl.off_core), st));
+  float* p2 = reinterpret_cast<float*>(ws_at(ws, bl.off_p2));
+  QSA_TRY(hip_status(qsa::launch_proj_gemm(attn, w_o, p2, T, bl.d_model, bl.hqd, bl.S2, st),
+                     "output projection launch"));
+  return hip_status(qsa::launch_proj_reduce(p2, bl.S2, (int64_t)T * bl.d_model, y, st),
+                    "output reduce launch");
+}
+
 }  // extern "C"
+

@@ -1,0 +1,263 @@
+// The QSA attention block around the hot path, for gfx950 (MI355X).
+//
+// The llama.cpp PR #27739 page, LocalAI QSA-block commit (opening paragraph)
+// lists the block end to end: q/k/v/o projections, q/k norms with the
+// (1 + w) weight polarity, RoPE, the indexer, the gather consumer, the
+// sigmoid output gate and o_proj; its fresh-review section has the query
+// side and the pooled indexer keys rotated with one set of angles.
+//
+// Kernels:
+//   proj_gemm   C = A . B^T for the projections (A [M][K] activations, B
+//               [N][K] Linear weights, both bf16 with K contiguous), on
+//               v_mfma_f32_16x16x32_bf16 with both operands loaded straight
+//               from memory (their MFMA layouts are 16 contiguous bytes of a
+//               row per lane).  A workgroup owns a 32x32 output tile; its four
+//               waves take interleaved k-steps of the workgroup's k range and
+//               are summed through LDS; the grid splits K further into fp32
+//               partials when the tiles alone cannot fill the chip (decode).
+//   block_prep  one workgroup per token: sums the partials of the stacked
+//               input projection, RMSNorm (1 + w) and RoPE on the q and k
+//               heads, RoPE on the indexer query heads, bf16 rounding of
+//               everything the QSA path reads; head weights all ones.
+//   proj_reduce sums the partials of o_proj into the bf16 output.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+#include "qsa_device.h"
+
+// ---------------------------------------------------------------------------
+// Projection GEMM.  Matrix-core layout of v_mfma_f32_16x16x32_bf16 (l = lane):
+//   A[i][k]: i = l%16, k = 8*(l/16) + e;  B[k][j]: j = l%16, k = 8*(l/16) + e;
+//   C[i][j]: j = l%16, i = 4*(l/16) + r.
+// A lane's A fragment is 16 bytes of activation row (m0 + l%16) at column
+// k0 + 8*(l/16); its B fragment 16 bytes of weight row (n0 + l%16) there too.
+constexpr int kGemmSteps = 8;  // k-steps (32 wide) a wave requests at once
+// Offset of a row past the matrix: every offset from here on is past the end
+// (the host keeps both operands under 2 GiB), also after adding a k offset.
+constexpr uint32_t kGemmOob = 0x80000000u;
+
+__global__ __launch_bounds__(256) void proj_gemm_kernel(const uint16_t* __restrict__ A,
+                                                        const uint16_t* __restrict__ B,
+                                                        float* __restrict__ part, int M, int N,
+                                                        int K, int k_split) {
+  __shared__ float red[4][32][33];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32, s = blockIdx.z;
+  const int kb = s * k_split, ke = min(K, kb + k_split);
+  const int nsteps = (ke - kb) >> 5;  // k_split and K are multiples of 32
+  const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A, (uint32_t)((int64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(B, (uint32_t)((int64_t)N * K * 2));
+  // Row offsets (bytes) of this lane's two A rows and two B rows; rows past
+  // the matrix read past the end of the buffer and come back zero.
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + 16 * i + c16, n = n0 + 16 * i + c16;
+    aoff[i] = m < M ? (uint32_t)(m * K + 8 * q4) * 2u : kGemmOob;
+    boff[i] = n < N ? (uint32_t)(n * K + 8 * q4) * 2u : kGemmOob;
+  }
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  // Wave wid takes k-steps wid, wid + 4, wid + 8, ... of [kb, ke).
+  for (int st0 = wid; st0 < nsteps; st0 += 4 * kGemmSteps) {
+    uint4 af[kGemmSteps][2], bfr[kGemmSteps][2];
+#pragma unroll
+    for (int u = 0; u < kGemmSteps; ++u) {
+      const int stp = st0 + 4 * u;
+      const uint32_t kbyte = (uint32_t)(kb + 32 * stp) * 2u;
+      const bool live = stp < nsteps;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[u][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ars, live ? aoff[i] + kbyte : kGemmOob, 0, 0));
+        bfr[u][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  brs, live ? boff[i] + kbyte : kGemmOob, 0, 0));
+      }
+    }
+    // All of this round's loads are in flight before the first MFMA.  (Steps
+    // past the range loaded zeros: their products add nothing.)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kGemmSteps; ++u) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8_t, af[u][i]), __builtin_bit_cast(bf16x8_t, bfr[u][j]),
+              acc[i][j], 0, 0, 0);
+    }
+  }
+  // C fragment: row 16 i + 4 q4 + r, column 16 j + c16.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wid][16 * i + 4 * q4 + r][16 * j + c16] = acc[i][j][r];
+  __syncthreads();
+  // Sum the four waves (in wave order) and store this split's partial tile.
+  float* P = part + (int64_t)s * M * N;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = threadIdx.x + 256 * e, rr = idx >> 5, cc = idx & 31;
+    const int m = m0 + rr, n = n0 + cc;
+    const float v = ((red[0][rr][cc] + red[1][rr][cc]) + red[2][rr][cc]) + red[3][rr][cc];
+    if (m < M && n < N) P[(int64_t)m * N + n] = v;
+  }
+}
+
+// Sum of the S partials of element (m, n), splits in order.
+__device__ __forceinline__ float sum_parts(const float* part, int S, int64_t MN, int64_t idx) {
+  float v = 0.0f;
+  for (int s = 0; s < S; ++s) v += part[s * MN + idx];
+  return v;
+}
+
+__global__ __launch_bounds__(256) void proj_reduce_kernel(const float* __restrict__ part, int S,
+                                                          int64_t MN,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx < MN) out[idx] = bf16_rne(sum_parts(part, S, MN, idx));
+}
+
+struct QueryPosB {
+  int p;
+  bool ok;
+};
+// Position of new token t (cu_q / past_len, as the rest of the path).
+__device__ QueryPosB token_pos(const Geo& g, int t) {
+  int lo = 0, hi = g.B - 1;
+  while (lo < hi) {  // last b with cu_q[b] <= t
+    const int mid = (lo + hi + 1) >> 1;
+    if (g.cu_q[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  const int b = lo, p = g.past_len[b] + (t - g.cu_q[b]);
+  return {p, p >= 0 && p < g.cap};
+}
+
+// One workgroup per token.  Rows of the stacked input projection, one wave
+// per row at a time: q heads, gate heads, k heads, v heads, indexer-query
+// heads, the indexer key.  Lane l holds values l and l + 64 of a row.
+__global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a) {
+  __shared__ float rowbuf[4][128];
+  const int t = blockIdx.x, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const QueryPosB qp = token_pos(g, t);
+  const int64_t pos = qp.ok ? qp.p : 0;
+  const int D = g.D, Hq = g.Hq, Hkv = g.Hkv, HI = g.HI, dI = g.dI;
+  const int n_rows = 2 * Hq + 2 * Hkv + (g.r > 0 ? HI + 1 : 0);
+  const int64_t MN = (int64_t)g.T * a.n_in;
+  const float* P = a.part + (int64_t)t * a.n_in;
+  float* row = rowbuf[wid];
+  for (int rw = wid; rw < n_rows; rw += 4) {
+    int kind, head, base, len;  // kind: 0 q, 1 gate, 2 k, 3 v, 4 indexer q, 5 indexer k
+    if (rw < Hq) { kind = 0; head = rw; base = head * D; len = D; }
+    else if (rw < 2 * Hq) { kind = 1; head = rw - Hq; base = (Hq + head) * D; len = D; }
+    else if (rw < 2 * Hq + Hkv) { kind = 2; head = rw - 2 * Hq; base = (2 * Hq + head) * D; len = D; }
+    else if (rw < 2 * Hq + 2 * Hkv) {
+      kind = 3; head = rw - 2 * Hq - Hkv; base = (2 * Hq + Hkv + head) * D; len = D;
+    } else if (rw < 2 * Hq + 2 * Hkv + HI) {
+      kind = 4; head = rw - 2 * Hq - 2 * Hkv; base = (2 * Hq + 2 * Hkv) * D + head * dI; len = dI;
+    } else {
+      kind = 5; head = 0; base = (2 * Hq + 2 * Hkv) * D + HI * dI; len = dI;
+    }
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = lane + 64 * e;
+      v[e] = x < len ? sum_parts(P, a.S, MN, base + x) : 0.0f;
+    }
+    if (kind == 0 || kind == 2) {
+      // RMSNorm over the head, weight (1 + w).
+      const float ss = wave_sum(v[0] * v[0] + v[1] * v[1]);
+      const float inv = 1.0f / sqrtf(ss / (float)len + a.eps);
+      const uint16_t* w = kind == 0 ? a.q_norm : a.k_norm;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int x = lane + 64 * e;
+        if (x < len) v[e] = (v[e] * inv) * (1.0f + to_f32(w[x]));
+      }
+    }
+    if (kind == 0 || kind == 2 || kind == 4) {
+      const int R = kind == 4 ? g.idx_rope_dim : a.rotary_dim;
+      if (R > 0) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          if (lane + 64 * e < len) row[lane + 64 * e] = v[e];
+        wave_sync();
+        float rv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int x = lane + 64 * e;
+          // (one call per table: no pointer chosen at run time)
+          rv[e] = x >= len ? 0.0f
+                  : kind == 4 ? rope_at(row, x, R, g.idx_freq, pos)
+                              : rope_at(row, x, R, a.freq, pos);
+        }
+        wave_sync();  // the row is read before the next one is written
+        v[0] = rv[0];
+        v[1] = rv[1];
+      }
+    }
+    uint16_t* dst;
+    switch (kind) {
+      case 0: dst = a.q + ((int64_t)t * Hq + head) * D; break;
+      case 1: dst = a.gate + ((int64_t)t * Hq + head) * D; break;
+      case 2: dst = a.k + ((int64_t)t * Hkv + head) * D; break;
+      case 3: dst = a.v + ((int64_t)t * Hkv + head) * D; break;
+      case 4: dst = a.q_idx + ((int64_t)t * HI + head) * dI; break;
+      default: dst = a.k_idx + (int64_t)t * dI; break;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = lane + 64 * e;
+      if (x < len) dst[x] = bf16_rne(v[e]);
+    }
+  }
+  if (g.r > 0 && threadIdx.x < HI) a.w[(int64_t)t * HI + threadIdx.x] = 1.0f;
+}
+
+}  // namespace
+
+int gemm_splits(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + 31) / 32) * ((N + 31) / 32);
+  int64_t S = (768 + tiles - 1) / tiles;
+  S = std::max<int64_t>(1, std::min<int64_t>(S, K / 128));
+  const int64_t ks = ((K + S - 1) / S + 127) / 128 * 128;
+  return (int)((K + ks - 1) / ks);
+}
+
+int gemm_k_split(int K, int S) { return (int)(((K + S - 1) / S + 127) / 128 * 128); }
+
+hipError_t launch_proj_gemm(const void* A, const void* B, float* part, int M, int N, int K, int S,
+                            hipStream_t st) {
+  const int ks = gemm_k_split(K, S);
+  dim3 grid((N + 31) / 32, (M + 31) / 32, S);
+  proj_gemm_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A),
+                                         static_cast<const uint16_t*>(B), part, M, N, K, ks);
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, hipStream_t st) {
+  proj_reduce_kernel<<<(unsigned)((MN + 255) / 256), 256, 0, st>>>(part, S, MN,
+                                                                   static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st) {
+  block_prep_kernel<<<g.T, 256, 0, st>>>(g, a);
+  return hipGetLastError();
+}
+
+}  // namespace qsa

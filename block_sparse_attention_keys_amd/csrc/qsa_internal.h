@@ -27,6 +27,9 @@ struct Geo {
   int32_t kv_esz;              // bytes per K/V cache element
   float inv_k_scale, inv_v_scale;  // 8-bit: 1 / scale, the factor applied before encoding
   float out_scale;             // 8-bit: V scale (and 1/D when rotated) on the attention output
+  int32_t idx_rope_dim;        // > 0: each pooled key's first idx_rope_dim values are rotated
+                               // at its block's first position
+  double idx_freq[64];         // their rotary frequencies theta^(-2i/idx_rope_dim), fp64
   const int32_t* cu_q;
   const int32_t* past_len;
   const int32_t* page_table;
@@ -78,6 +81,31 @@ hipError_t launch_attend(const Geo& g, int elem, const AttnPlan& plan, const voi
                          const void* k_cache, const void* v_cache, const int32_t* sel,
                          const int32_t* n_blocks, const void* gate, void* out, float* part,
                          hipStream_t st, const InKernelSelect& fs = InKernelSelect{});
+
+// The block front end (projections, norms, RoPE) and o_proj.
+struct BlockPrepArgs {
+  const float* part;           // [S][T][n_in] fp32 partials of the stacked input projection
+  int32_t S, n_in;
+  float eps;                   // RMSNorm epsilon
+  int32_t rotary_dim;          // rotated values of each q / k head (rotate-half)
+  double freq[64];             // their frequencies theta^(-2i/rotary_dim), fp64
+  const uint16_t* q_norm;      // [D] bf16, applied as (1 + w)
+  const uint16_t* k_norm;
+  uint16_t* q;                 // [T][Hq][D] bf16 outputs
+  uint16_t* gate;              // [T][Hq][D]
+  uint16_t* k;                 // [T][Hkv][D]
+  uint16_t* v;                 // [T][Hkv][D]
+  uint16_t* q_idx;             // [T][H_I][d_I]
+  uint16_t* k_idx;             // [T][d_I]
+  float* w;                    // [T][H_I], all ones
+};
+// Split count and k range per split of a projection GEMM of M x N x K.
+int gemm_splits(int M, int N, int K);
+int gemm_k_split(int K, int S);
+hipError_t launch_proj_gemm(const void* A, const void* B, float* part, int M, int N, int K, int S,
+                            hipStream_t st);
+hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, hipStream_t st);
+hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st);
 
 // True when a kernel instantiation exists for G heads per KV head and dim D.
 bool attend_supported(int G, int D);

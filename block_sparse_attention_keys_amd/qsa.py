@@ -26,7 +26,8 @@ QSA_KV_SAME = 0
 QSA_KV_FP8 = 2
 
 EXPORTS = ["qsa_last_error", "qsa_pooled_ld", "qsa_workspace_size", "qsa_pool_keys",
-           "qsa_store_kv", "qsa_score_select", "qsa_attend", "qsa_forward"]
+           "qsa_store_kv", "qsa_score_select", "qsa_attend", "qsa_forward",
+           "qsa_block_workspace_size", "qsa_block_forward"]
 
 
 class qsa_params(C.Structure):
@@ -34,7 +35,13 @@ class qsa_params(C.Structure):
                 ("n_idx_heads", C.c_int32), ("idx_dim", C.c_int32), ("block_size", C.c_int32),
                 ("ratio", C.c_int32), ("budget", C.c_int32), ("attn_scale", C.c_float),
                 ("idx_scale", C.c_float), ("dtype", C.c_int32), ("kv_dtype", C.c_int32),
-                ("kv_rotate", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float)]
+                ("kv_rotate", C.c_int32), ("k_scale", C.c_float), ("v_scale", C.c_float),
+                ("idx_rope_dim", C.c_int32), ("idx_rope_theta", C.c_float)]
+
+
+class qsa_block_params(C.Structure):
+    _fields_ = [("d_model", C.c_int32), ("rotary_dim", C.c_int32), ("rope_theta", C.c_float),
+                ("norm_eps", C.c_float)]
 
 
 class qsa_batch(C.Structure):
@@ -80,6 +87,11 @@ def lib(path: str = LIB_PATH) -> C.CDLL:
     L.qsa_attend.argtypes = [P, B, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
     L.qsa_forward.restype = C.c_int
     L.qsa_forward.argtypes = [P, B] + [vp] * 15 + [C.c_size_t, vp]
+    BP = C.POINTER(qsa_block_params)
+    L.qsa_block_workspace_size.restype = C.c_size_t
+    L.qsa_block_workspace_size.argtypes = [P, BP, B]
+    L.qsa_block_forward.restype = C.c_int
+    L.qsa_block_forward.argtypes = [P, BP, B] + [vp] * 13 + [C.c_size_t, vp]
     _lib = L
     return L
 
@@ -118,10 +130,12 @@ def last_error() -> str:
 
 def make_params(n_q_heads, n_kv_heads, head_dim, n_idx_heads, idx_dim, block_size, budget,
                 dtype, ratio=None, attn_scale=0.0, idx_scale=0.0, kv_dtype=QSA_KV_SAME,
-                kv_rotate=0, k_scale=1.0, v_scale=1.0) -> qsa_params:
+                kv_rotate=0, k_scale=1.0, v_scale=1.0, idx_rope_dim=0,
+                idx_rope_theta=0.0) -> qsa_params:
     return qsa_params(n_q_heads, n_kv_heads, head_dim, n_idx_heads, idx_dim, block_size,
                       block_size if ratio is None else ratio, budget, attn_scale, idx_scale,
-                      dtype, kv_dtype, kv_rotate, k_scale, v_scale)
+                      dtype, kv_dtype, kv_rotate, k_scale, v_scale, idx_rope_dim,
+                      idx_rope_theta)
 
 
 class Batch:
@@ -178,3 +192,22 @@ def qsa_forward(params, batch, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cac
                              _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(pooled),
                              _ptr(out), _ptr(sel), _ptr(n_blocks), _ptr(ws), _nbytes(ws),
                              _stream(stream)))
+
+
+def make_block_params(d_model, rotary_dim, rope_theta, norm_eps=1e-6) -> qsa_block_params:
+    return qsa_block_params(d_model, rotary_dim, rope_theta, norm_eps)
+
+
+def qsa_block_workspace_size(params: qsa_params, block: qsa_block_params, batch) -> int:
+    return int(lib().qsa_block_workspace_size(C.byref(params), C.byref(block),
+                                              C.byref(_b(batch))))
+
+
+def qsa_block_forward(params, block, batch, x, w_in, q_norm, k_norm, w_o, k_cache, v_cache,
+                      k_idx_cache, pooled, y, sel=None, n_blocks=None, ws=None,
+                      stream=None) -> None:
+    _check(lib().qsa_block_forward(C.byref(params), C.byref(block), C.byref(_b(batch)), _ptr(x),
+                                   _ptr(w_in), _ptr(q_norm), _ptr(k_norm), _ptr(w_o),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(pooled),
+                                   _ptr(y), _ptr(sel), _ptr(n_blocks), _ptr(ws), _nbytes(ws),
+                                   _stream(stream)))

@@ -41,7 +41,7 @@ class DeviceCase:
                  idx_scale: float = 0.0, budget: Optional[int] = None,
                  block_size: Optional[int] = None, page_offset: int = 0,
                  kv_fp8: Optional[bool] = None, kv_rotate: Optional[bool] = None,
-                 kv_scale: Optional[tuple] = None):
+                 kv_scale: Optional[tuple] = None, idx_rope: tuple = (0, 0.0)):
         sp = case.spec
         self.case, self.spec, self.device = case, sp, torch.device(device)
         self.dt = torch.bfloat16 if sp.dtype == BF16 else torch.float32
@@ -62,7 +62,8 @@ class DeviceCase:
                                       attn_scale=attn_scale, idx_scale=idx_scale,
                                       kv_dtype=qsa.QSA_KV_FP8 if self.kv8 else qsa.QSA_KV_SAME,
                                       kv_rotate=int(self.kv_rotate), k_scale=self.k_scale,
-                                      v_scale=self.v_scale)
+                                      v_scale=self.v_scale, idx_rope_dim=idx_rope[0],
+                                      idx_rope_theta=idx_rope[1])
         self.n_tok = [int(x.shape[0]) for x in case.k]
         cap_tok = max(self.n_tok) + extra_steps
         self.paged = (layout or ("paged" if sp.page_size else "contiguous")) == "paged"
@@ -227,3 +228,82 @@ class DeviceCase:
                         inp["qI"], inp["kI_new"], inp["w"], inp["gate"], st["k"], st["v"],
                         st.get("kI"), st.get("pooled"), outs["out"], outs["sel"],
                         outs["n_blocks"], outs["ws"], stream)
+
+
+class BlockDeviceCase:
+    """Caches (empty at first), weights and per-call inputs of a QSA block
+    workload on one GPU; every call goes through qsa_block_forward.  The
+    context is filled by the block's own prefill calls."""
+
+    def __init__(self, bc, device="cuda", layout: str = "paged", page_size: int = 64):
+        sp = bc.spec
+        self.bc, self.spec, self.device = bc, sp, torch.device(device)
+        B = sp.n_seqs
+        self.B, self.r = B, sp.block_size
+        self.params = qsa.make_params(sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads,
+                                      sp.idx_dim, sp.block_size, sp.budget, qsa.QSA_BF16,
+                                      idx_rope_dim=bc.idx_rope_dim,
+                                      idx_rope_theta=bc.idx_rope_theta)
+        self.block = qsa.make_block_params(bc.d_model, bc.rotary_dim, bc.rope_theta, bc.norm_eps)
+        Hkv, D, dI = sp.n_kv_heads, sp.head_dim, sp.idx_dim
+        n_tok = bc.n_tok
+        self.paged = layout == "paged"
+        self.page_size = page_size
+        if self.paged:
+            ps = page_size
+            need = [_round(n, ps) // ps for n in n_tok]
+            self.max_pages = max(need)
+            self.cap = self.max_pages * ps
+            self.n_pages = int(sum(need))
+            perm = np.random.default_rng(4321).permutation(self.n_pages).astype(np.int32)
+            pt = np.full((B, self.max_pages), -1, np.int32)
+            o = 0
+            for b in range(B):
+                pt[b, :need[b]] = perm[o:o + need[b]]
+                o += need[b]
+            self.page_table = torch.from_numpy(pt).to(self.device)
+            kv_shape, ki_shape = (self.n_pages, Hkv, ps, D), (self.n_pages, ps, dI)
+        else:
+            self.cap = _round(max(n_tok), 64)
+            self.max_pages = self.n_pages = 0
+            self.page_table = None
+            kv_shape, ki_shape = (B, Hkv, self.cap, D), (B, self.cap, dI)
+        bf = torch.bfloat16
+        self.st = {"k": torch.zeros(kv_shape, dtype=bf, device=self.device),
+                   "v": torch.zeros(kv_shape, dtype=bf, device=self.device)}
+        if self.r > 0:
+            self.st["kI"] = torch.zeros(ki_shape, dtype=bf, device=self.device)
+            ld = qsa.qsa_pooled_ld(self.params, self.batch_for([0] * B, [1] * B))
+            self.st["pooled"] = torch.zeros((B, dI, ld), dtype=torch.float32, device=self.device)
+        dev = lambda a: _dev(a, self.device, BF16)  # noqa: E731
+        self.w_in, self.w_o = dev(bc.w_in), dev(bc.w_o)
+        self.q_norm, self.k_norm = dev(bc.q_norm), dev(bc.k_norm)
+
+    def batch_for(self, past: List[int], n_new: List[int]) -> qsa.Batch:
+        cu = np.zeros(self.B + 1, np.int32)
+        cu[1:] = np.cumsum(n_new)
+        T = int(cu[-1])
+        return qsa.Batch(self.B, T, max(1, max(n_new)), max(p + n for p, n in zip(past, n_new)),
+                         self.cap, torch.from_numpy(cu).to(self.device),
+                         torch.from_numpy(np.asarray(past, np.int32)).to(self.device),
+                         self.page_table, self.page_size if self.paged else 0, self.max_pages,
+                         self.n_pages)
+
+    def call_inputs(self, i: int) -> dict:
+        spans = self.bc.calls[i]
+        x = np.concatenate([self.bc.x[b][s:e] for b, (s, e) in enumerate(spans)], 0)
+        batch = self.batch_for([s for s, _ in spans], [e - s for s, e in spans])
+        T = int(x.shape[0])
+        k = max(1, self.params.budget // self.r if self.r else 1)
+        ws = max(qsa.qsa_block_workspace_size(self.params, self.block, batch), 16)
+        return {"x": _dev(x, self.device, BF16), "batch": batch, "T": T, "spans": spans,
+                "y": torch.empty((T, self.bc.d_model), dtype=torch.bfloat16, device=self.device),
+                "sel": torch.empty((T, k), dtype=torch.int32, device=self.device),
+                "n_blocks": torch.empty((T,), dtype=torch.int32, device=self.device),
+                "ws": torch.zeros((ws,), dtype=torch.uint8, device=self.device)}
+
+    def forward(self, c: dict, stream=None) -> None:
+        st = self.st
+        qsa.qsa_block_forward(self.params, self.block, c["batch"], c["x"], self.w_in, self.q_norm,
+                              self.k_norm, self.w_o, st["k"], st["v"], st.get("kI"),
+                              st.get("pooled"), c["y"], c["sel"], c["n_blocks"], c["ws"], stream)

@@ -323,3 +323,105 @@ def _draw(sp: Spec, seed: int) -> Case:
                 gate=[o[6] for o in out], q_pos=[o[7] for o in out], ctx=ctx,
                 planted=[o[8] for o in out], calls=calls,
                 page_table=page_table, n_pages=n_pages)
+
+
+# --------------------------------------------------------------------------
+# The QSA attention block around the path: hidden states and weights.
+# Hidden states x ~ N(0,1) (the block's input is normalised); Linear weights
+# ~ N(0, 1/fan_in) so that projections have unit variance; norm weights
+# ~ 0.1 N(0,1) (applied as 1 + w).  All bf16.
+
+@dataclasses.dataclass
+class BlockCase:
+    """A QSA block workload.  spec: the core dims and the batch shape;
+    x[b] [n_tok_b][d_model] bf16 bits; weights as bf16 bits: w_in [n_in][d_model]
+    (rows q, gate, k, v, indexer q, indexer k), q_norm / k_norm [D],
+    w_o [d_model][Hq*D].  calls: per call, one (start, end) span per sequence
+    (prefill chunks of the context, then one-token decode steps)."""
+
+    spec: Spec
+    d_model: int
+    rotary_dim: int
+    rope_theta: float
+    idx_rope_dim: int
+    idx_rope_theta: float
+    norm_eps: float
+    x: List[np.ndarray]
+    w_in: np.ndarray
+    q_norm: np.ndarray
+    k_norm: np.ndarray
+    w_o: np.ndarray
+    ctx: List[int]
+    calls: List[List[tuple]]
+
+    @property
+    def n_tok(self) -> List[int]:
+        return [int(a.shape[0]) for a in self.x]
+
+    def dims(self) -> dict:
+        sp = self.spec
+        return dict(n_q_heads=sp.n_q_heads, n_kv_heads=sp.n_kv_heads, head_dim=sp.head_dim,
+                    n_idx_heads=sp.n_idx_heads, idx_dim=sp.idx_dim, block_size=sp.block_size,
+                    budget=sp.budget, attn_scale=0.0, idx_scale=0.0,
+                    idx_rope_dim=self.idx_rope_dim, idx_rope_theta=self.idx_rope_theta,
+                    rotary_dim=self.rotary_dim, rope_theta=self.rope_theta,
+                    norm_eps=self.norm_eps)
+
+
+def block_n_in(sp: Spec) -> int:
+    n = 2 * sp.n_q_heads * sp.head_dim + 2 * sp.n_kv_heads * sp.head_dim
+    if sp.block_size > 0:
+        n += sp.n_idx_heads * sp.idx_dim + sp.idx_dim
+    return n
+
+
+def make_block_case(name: str, seed: int = 0, *, d_model: int = 2560, rotary_dim: int = 64,
+                    rope_theta: float = 1e7, idx_rope_dim: Optional[int] = None,
+                    norm_eps: float = 1e-6, chunk: int = 2048, decode_steps: int = 2,
+                    n_seqs: Optional[int] = None, ctx_range: Optional[tuple] = None,
+                    ctx: Optional[int] = None, budget: Optional[int] = None) -> BlockCase:
+    """The block over workload ``name``'s shape (heads, block size, budget,
+    contexts): each sequence's context arrives in prefill chunks of `chunk`
+    tokens, then `decode_steps` single-token steps follow."""
+    sp = SPECS[name]
+    repl = {}
+    if n_seqs is not None:
+        repl["n_seqs"] = n_seqs
+    if ctx_range is not None:
+        repl["ctx_lo"], repl["ctx_hi"] = ctx_range
+    if ctx is not None:
+        repl["ctx"], repl["ctx_lo"], repl["ctx_hi"] = ctx, 0, 0
+    if budget is not None:
+        repl["budget"] = budget
+    if repl:
+        sp = dataclasses.replace(sp, **repl)
+    root = np.random.SeedSequence(seed)
+    meta_rng, w_rng, *seq_seeds = [np.random.default_rng(s) for s in root.spawn(2 + sp.n_seqs)]
+    B = sp.n_seqs
+    if sp.ctx_hi > 0:
+        ctxs = [int(c) for c in meta_rng.integers(sp.ctx_lo, sp.ctx_hi + 1, size=B)]
+    elif sp.kind == "prefill":
+        ctxs = [sp.prefill_len] * B
+    else:
+        ctxs = [sp.ctx] * B
+    n_tok = [c + decode_steps for c in ctxs]
+    x = [bf16_bits(r.standard_normal((n, d_model), dtype=np.float32))
+         for r, n in zip(seq_seeds, n_tok)]
+    n_in = block_n_in(sp)
+    hqd = sp.n_q_heads * sp.head_dim
+    w_in = bf16_bits(w_rng.standard_normal((n_in, d_model), dtype=np.float32)
+                     * np.float32(d_model ** -0.5))
+    q_norm = bf16_bits(w_rng.standard_normal(sp.head_dim, dtype=np.float32) * np.float32(0.1))
+    k_norm = bf16_bits(w_rng.standard_normal(sp.head_dim, dtype=np.float32) * np.float32(0.1))
+    w_o = bf16_bits(w_rng.standard_normal((d_model, hqd), dtype=np.float32)
+                    * np.float32(hqd ** -0.5))
+    calls: List[List[tuple]] = []
+    for s in range(0, max(ctxs), chunk):
+        calls.append([(min(s, c), min(s + chunk, c)) for c in ctxs])
+    for i in range(decode_steps):
+        calls.append([(c + i, c + i + 1) for c in ctxs])
+    idx_rope = (sp.idx_dim if idx_rope_dim is None else idx_rope_dim) if sp.block_size > 0 else 0
+    return BlockCase(spec=sp, d_model=d_model, rotary_dim=rotary_dim, rope_theta=rope_theta,
+                     idx_rope_dim=idx_rope, idx_rope_theta=rope_theta if idx_rope else 0.0,
+                     norm_eps=norm_eps, x=x, w_in=w_in, q_norm=q_norm, k_norm=k_norm, w_o=w_o,
+                     ctx=ctxs, calls=calls)

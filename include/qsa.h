@@ -112,6 +112,15 @@ typedef struct {
                           (needs Hq/Hkv >= 4) */
   float k_scale;       /* QSA_KV_FP8: scale of the K codes (> 0) */
   float v_scale;       /* QSA_KV_FP8: scale of the V codes (> 0) */
+  int32_t idx_rope_dim;   /* rotary indexer keys: 0 = none; else an even number <= d_I.
+                             Each pooled key's first idx_rope_dim values are rotated at
+                             the block's first position j*r (rotate-half RoPE, frequencies
+                             idx_rope_theta^(-2i/idx_rope_dim), angle and its cosine/sine
+                             in fp64 rounded to fp32, rotation in fp32).  The caller's
+                             q_idx must be rotated the same way at its own position
+                             (qsa_block_forward does it).  LocalAI QSA-block commit: RoPE on
+                             the indexer query and pooled keys, one set of angles. */
+  float idx_rope_theta;   /* base of those frequencies (> 0 when idx_rope_dim > 0) */
 } qsa_params;
 
 /* One call's batch (host sizes for launch geometry + device metadata). */
@@ -151,16 +160,16 @@ size_t qsa_workspace_size(const qsa_params* params, const qsa_batch* batch);
  * in fp32.  Only new blocks are touched, O(new tokens) -- not the whole-cache
  * recompute of the upstream reference ("The trap the layer loop walks into").
  * Dense layer (block_size 0): QSA_ERR_INVALID. */
+qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,
+                         const void* k_idx_new, void* k_idx_cache, float* pooled,
+                         void* stream);
+
 /* K/V append only: writes k_new[t], v_new[t] to rows past_len[b] + (t -
  * cu_q[b]) of k_cache / v_cache under the layer's storage (QSA_KV_FP8: rotated
  * if asked, scaled and encoded as above).  For filling a cache with context
  * rows; qsa_forward appends its own new rows. */
 qsa_status qsa_store_kv(const qsa_params* params, const qsa_batch* batch, const void* k_new,
                         const void* v_new, void* k_cache, void* v_cache, void* stream);
-
-qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,
-                         const void* k_idx_new, void* k_idx_cache, float* pooled,
-                         void* stream);
 
 /* Block scoring and top-k selection (steps 2-3 above).
  * Reads q_idx [T][H_I][d_I], w [T][H_I] and the pooled cache; writes sel and
@@ -190,6 +199,52 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
                        void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
                        void* out, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * The QSA attention block around the path (llama.cpp PR #27739 page,
+ * LocalAI QSA-block commit, opening paragraph: q/k/v/o projections, the
+ * (1 + w) q/k norms, RoPE, the indexer, the gather consumer, the sigmoid
+ * output gate and o_proj; fresh-review section: one set of rotary angles for
+ * the query side and the pooled indexer keys).
+ *
+ * Readings where the pages are silent:
+ *   - weights are Linear [out][in] bf16; w_in stacks the rows of the q (Hq*D),
+ *     gate (Hq*D), k (Hkv*D), v (Hkv*D), indexer-query (H_I*d_I) and
+ *     indexer-key (d_I) projections, in that order (a dense layer has no
+ *     indexer rows); w_o is [d_model][Hq*D];
+ *   - q/k norm: RMSNorm over each head's D values, x / sqrt(mean(x^2) + eps)
+ *     * (1 + w) with one [D] bf16 weight shared by the heads;
+ *   - RoPE (rotate-half) on the first rotary_dim values of each q and k head
+ *     at the token's position; the indexer query with idx_rope_dim /
+ *     idx_rope_theta of qsa_params, the pooled keys as documented there;
+ *   - indexer head weights all ones, no indexer norm; the gate is its own
+ *     projection, sigmoid-applied elementwise. */
+typedef struct {
+  int32_t d_model;     /* hidden size, a multiple of 32 */
+  int32_t rotary_dim;  /* rotated values per q/k head, even, <= head_dim */
+  float rope_theta;    /* RoPE base (> 0 when rotary_dim > 0) */
+  float norm_eps;      /* RMSNorm epsilon (>= 0) */
+} qsa_block_params;
+
+/* Workspace bytes of qsa_block_forward for this call (0 on invalid
+ * arguments or n_tokens == 0). */
+size_t qsa_block_workspace_size(const qsa_params* params, const qsa_block_params* block,
+                                const qsa_batch* batch);
+
+/* One QSA block step for the batch's new tokens: x [T][d_model] bf16 hidden
+ * states -> y [T][d_model] bf16.  Projections on bf16 matrix cores with fp32
+ * accumulation; q, gate, k, v, indexer q and k rounded to bf16 after the
+ * norm and RoPE; then the QSA step of qsa_forward (append K/V and indexer
+ * keys at past_len, pool, score, select, attend, gate) on those tensors;
+ * then o_proj of the bf16 attention output.  q_norm / k_norm: [D] bf16.
+ * Caches, pooled cache, selections and errors as qsa_forward; ws:
+ * qsa_block_workspace_size bytes, 16-byte aligned.  dtype must be QSA_BF16. */
+qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* block,
+                             const qsa_batch* batch, const void* x, const void* w_in,
+                             const void* q_norm, const void* k_norm, const void* w_o,
+                             void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                             void* y, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
+                             size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ def dims_of(dc: runner.DeviceCase) -> dict:
     p = dc.params
     return dict(n_q_heads=p.n_q_heads, n_kv_heads=p.n_kv_heads, head_dim=p.head_dim,
                 n_idx_heads=p.n_idx_heads, idx_dim=p.idx_dim, block_size=p.block_size,
-                budget=p.budget, attn_scale=p.attn_scale, idx_scale=p.idx_scale)
+                budget=p.budget, attn_scale=p.attn_scale, idx_scale=p.idx_scale,
+                idx_rope_dim=p.idx_rope_dim, idx_rope_theta=p.idx_rope_theta)
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:

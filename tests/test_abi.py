@@ -40,6 +40,14 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, n), n
 
 
+def test_binding_argument_counts_match_header(L):
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in declared_functions():
+        m = re.search(name + r"\s*\(([^)]*)\)", text)
+        params = [q for q in m.group(1).split(",") if q.strip() and q.strip() != "void"]
+        assert len(getattr(L, name).argtypes) == len(params), name
+
+
 def test_struct_layouts_match_header():
     # field order and sizes of the ctypes mirrors against the header text
     text = open(HEADER).read()
@@ -50,6 +58,15 @@ def test_struct_layouts_match_header():
     body = text[text.index("} qsa_params;"):text.index("} qsa_batch;")]
     names = re.findall(r"(?:int32_t|const int32_t\s*\*)\s*(\w+);", body)
     assert names == [f for f, _ in qsa.qsa_batch._fields_]
+
+
+def test_block_struct_layout_matches_header():
+    text = open(HEADER).read()
+    i = text.index("} qsa_batch;")
+    body = text[text.index("typedef struct {", i):text.index("} qsa_block_params;")]
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [f for _, f in fields] == [f for f, _ in qsa.qsa_block_params._fields_]
+    assert C.sizeof(qsa.qsa_block_params) == 4 * len(fields)
 
 
 def P(**kw):
@@ -155,6 +172,42 @@ def test_store_kv_validates(L):
                           None) == qsa.QSA_ERR_INVALID
     b = Bt(n_tokens=0, cu_q=None, past_len=None)
     assert L.qsa_store_kv(C.byref(p), C.byref(b), None, None, None, None, None) == qsa.QSA_OK
+
+
+@pytest.mark.parametrize("kw,bkw,status,needle", [
+    (dict(), dict(d_model=100), qsa.QSA_ERR_INVALID, "d_model"),
+    (dict(), dict(rotary_dim=130), qsa.QSA_ERR_INVALID, "rotary_dim"),
+    (dict(), dict(rotary_dim=7), qsa.QSA_ERR_INVALID, "rotary_dim"),
+    (dict(), dict(rope_theta=0.0), qsa.QSA_ERR_INVALID, "rope_theta"),
+    (dict(), dict(norm_eps=-1.0), qsa.QSA_ERR_INVALID, "norm_eps"),
+    (dict(dtype=qsa.QSA_F32), dict(), qsa.QSA_ERR_UNSUPPORTED, "QSA_BF16"),
+    (dict(idx_rope_dim=66), dict(), qsa.QSA_ERR_INVALID, "idx_rope_dim"),
+    (dict(idx_rope_dim=32, idx_rope_theta=0.0), dict(), qsa.QSA_ERR_INVALID, "idx_rope_theta"),
+    (dict(block_size=0, ratio=0, idx_rope_dim=32, idx_rope_theta=1e4), dict(),
+     qsa.QSA_ERR_INVALID, "dense"),
+])
+def test_block_params_rejected(L, kw, bkw, status, needle):
+    base = dict(d_model=512, rotary_dim=64, rope_theta=1e6, norm_eps=1e-6)
+    base.update(bkw)
+    bp = qsa.make_block_params(**base)
+    p = P(**kw)
+    rc = L.qsa_block_forward(C.byref(p), C.byref(bp), C.byref(Bt()), *([FAKE] * 13), 1 << 30, None)
+    assert rc == status
+    assert needle in qsa.last_error()
+    assert qsa.qsa_block_workspace_size(p, bp, Bt()) == 0
+
+
+def test_block_workspace_and_pointers(L):
+    p, bp = P(idx_rope_dim=64, idx_rope_theta=1e6), qsa.make_block_params(512, 64, 1e6)
+    need = qsa.qsa_block_workspace_size(p, bp, Bt())
+    assert need > qsa.qsa_workspace_size(p, Bt()) > 0
+    args = [FAKE] * 13
+    assert L.qsa_block_forward(C.byref(p), C.byref(bp), C.byref(Bt()), *args, need - 1,
+                               None) == qsa.QSA_ERR_WORKSPACE
+    args[0] = None
+    assert L.qsa_block_forward(C.byref(p), C.byref(bp), C.byref(Bt()), *args, need,
+                               None) == qsa.QSA_ERR_INVALID
+    assert "x is NULL" in qsa.last_error()
 
 
 def test_dense_layer_rejects_indexer_calls(L):

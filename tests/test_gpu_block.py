@@ -1,0 +1,159 @@
+"""The QSA block front end on the GPU (qsa_block_forward) and rotary indexer
+keys in the core path, against the CPU oracle (oracle/block.py and the
+sequence oracle with rotated pooled keys).
+
+Rotary indexer keys with the core entry points use seeded indexer inputs,
+so pooled keys, scores and selections compare bit for bit.  Through the
+block, the indexer inputs come out of bf16 projections (parity.py states the
+bar for that case)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from oracle import block as oblock
+from block_sparse_attention_keys_amd import qsa, runner, workloads
+from gpu_harness import SeqF32, check_call, pooled_rows, run_calls, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    qsa.lib()
+    yield
+
+
+ROPE = (64, 1e6)
+
+
+def _oracle_pooled(orc, kI, r, R, theta):
+    p = orc.pool(kI, r)
+    return orc.rope(p, R, theta, np.arange(p.shape[0]) * r)
+
+
+def test_rotated_pooled_keys_bitexact_prefill_and_decode():
+    """qsa_pool_keys on the context and the decode form's pooler on new
+    blocks both store the mean rotated at the block's first position, bit
+    for bit; decode outputs and selections match the oracle."""
+    case = workloads.make_case("ragged_paged_decode_128k_bf16", n_seqs=5, ctx_range=(1000, 6000),
+                               steps=70)
+    dc = runner.DeviceCase(case, idx_rope=ROPE)
+    orc = oracle.load()
+    got = pooled_rows(dc)
+    for b in range(case.spec.n_seqs):
+        ref = _oracle_pooled(orc, case.kI[b][:case.ctx[b]], 64, *ROPE)
+        assert np.array_equal(got[b, :ref.shape[0]], ref), f"context pooled keys of seq {b}"
+    res = run_calls(dc, keep={0, 35, 69})
+    seqf = SeqF32(case)
+    for i in sorted(res):
+        check_call(dc, seqf, res[i])
+    got = pooled_rows(dc)
+    for b in range(case.spec.n_seqs):
+        ref = _oracle_pooled(orc, case.kI[b], 64, *ROPE)
+        assert np.array_equal(got[b, :ref.shape[0]], ref), f"decoded pooled keys of seq {b}"
+
+
+def test_rotated_pooled_keys_chunked_prefill():
+    case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=3000 + 17, chunk=1000)
+    dc = runner.DeviceCase(case, idx_rope=(32, 5e5))
+    res = run_calls(dc, keep={0, 3})
+    seqf = SeqF32(case)
+    for i in sorted(res):
+        check_call(dc, seqf, res[i], sample=64, rng_seed=i)
+    ref = _oracle_pooled(oracle.load(), case.kI[0], 64, 32, 5e5)
+    assert np.array_equal(pooled_rows(dc)[0, :ref.shape[0]], ref)
+
+
+def _run_block(bc, layout="paged", keep=None):
+    dc = runner.BlockDeviceCase(bc, layout=layout)
+    res = {}
+    for i in range(len(bc.calls)):
+        c = dc.call_inputs(i)
+        say(f"  block call {i}/{len(bc.calls)}: T={c['T']}")
+        dc.forward(c)
+        torch.cuda.synchronize()
+        if keep is None or i in keep:
+            res[i] = (c["y"].float().cpu().numpy(), c["sel"].cpu().numpy(),
+                      c["n_blocks"].cpu().numpy(), c["spans"])
+    return dc, res
+
+
+def _check_block(bc, result, sample=None, seed=0):
+    orc = oracle.load()
+    y, sel, nblk, spans = result
+    dims = bc.dims()
+    r = dims["block_size"]
+    rng = np.random.default_rng(seed)
+    t0 = 0
+    rows = differ = 0
+    stats = None
+    for b, (s, e) in enumerate(spans):
+        n_q = e - s
+        if n_q == 0:
+            continue
+        idx = np.arange(n_q)
+        if sample is not None and n_q > sample:
+            idx = np.sort(rng.choice(n_q, size=sample, replace=False))
+        ref = oblock.block(orc, dims, bc.x[b][:e], bc.w_in, bc.q_norm, bc.k_norm, bc.w_o, s + idx,
+                           want_scores=r > 0)
+        same = np.ones(len(idx), bool)
+        if r > 0:
+            k = ref["sel"].shape[1]
+            verdict = parity.block_selection_rows(sel[t0 + idx][:, :k], nblk[t0 + idx], ref["sel"],
+                                                  ref["n_blocks"], ref["scores"],
+                                                  (s + idx + 1) // r)
+            assert (verdict >= 0).all(), f"seq {b}: invalid selection rows {np.where(verdict < 0)[0]}"
+            same = verdict == 0
+            differ += int((~same).sum())
+        rows += len(idx)
+        if same.any():
+            ok, stats = parity.outputs_ok(y[t0 + idx][same], ref["y"][same], "bf16")
+            assert ok, f"seq {b} block outputs {stats}"
+        t0 += n_q
+    assert differ <= parity.BLOCK_ROWS_DIFFERING * max(rows, 1), (differ, rows)
+    say(f"  rows {rows}, selections differing (valid) {differ}, last stats {stats}")
+
+
+def test_block_prefill_then_decode_paged():
+    """Ragged contexts filled by the block's own chunked prefill (2048-token
+    chunks, a ragged last chunk, sequences with no tokens in some calls),
+    then decode steps; d_model 512."""
+    bc = workloads.make_block_case("ragged_paged_decode_128k_bf16", d_model=512, n_seqs=4,
+                                   ctx_range=(700, 5000), chunk=2048, decode_steps=3)
+    _, res = _run_block(bc)
+    last = len(bc.calls) - 1
+    for i in sorted(res):
+        _check_block(bc, res[i], sample=None if i >= last - 2 else 96, seed=i)
+
+
+def test_block_contiguous_equals_paged_bitwise():
+    bc = workloads.make_block_case("ragged_paged_decode_128k_bf16", d_model=256, n_seqs=3,
+                                   ctx_range=(300, 2500), chunk=1024, decode_steps=2)
+    _, a = _run_block(bc, layout="paged")
+    _, b = _run_block(bc, layout="contiguous")
+    for i in a:
+        for x, z in zip(a[i][:3], b[i][:3]):
+            assert np.array_equal(x, z), f"call {i}"
+
+
+def test_block_released_width_decode():
+    """d_model 2560 (the released hidden size), one 32K-context sequence:
+    the prefill in 4096-token chunks and two decode steps, outputs and
+    selections of the decode steps against the oracle."""
+    bc = workloads.make_block_case("decode_32k_bf16", d_model=2560, chunk=4096, decode_steps=2)
+    _, res = _run_block(bc, keep={len(bc.calls) - 2, len(bc.calls) - 1})
+    for i in sorted(res):
+        _check_block(bc, res[i])
+
+
+def test_block_dense_layer():
+    """Block size 0: no indexer rows in the input projection."""
+    bc = workloads.make_block_case("mtp_dense_ragged_bf16", d_model=512, n_seqs=3,
+                                   ctx_range=(500, 3000), chunk=1024, decode_steps=2)
+    _, res = _run_block(bc)
+    for i in sorted(res):
+        _check_block(bc, res[i], sample=48, seed=i)
