@@ -38,7 +38,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ragged_paged_decode_128k_bf16")
     ap.add_argument("--layers", type=int, default=0, help="cache copies to rotate over (0 = auto)")
@@ -86,6 +86,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     name = args.workload
+    if name in BLOCK_BENCH:
+        return bench_block(args, name)
     sp = workloads.SPECS[name]
     if sp.kind != "decode":
         return bench_prefill(args, name)
@@ -220,6 +222,102 @@ def main():
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case, sp, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+# The QSA block (projections, norms, RoPE, QSA, o_proj) over a decode workload.
+BLOCK_BENCH = {
+    "block_ragged_paged_decode_128k": dict(spec="ragged_paged_decode_128k_bf16", d_model=2560,
+                                           rotary_dim=64, rope_theta=1e7, idx_rope_dim=64),
+}
+
+
+def bench_block(args, name):
+    """One decode step of the QSA block per sequence (qsa_block_forward): a
+    step is the whole block for B new tokens.  Hidden states, weights (one
+    copy per layer copy of the caches) and the per-step inputs are drawn on
+    the GPU; the caches hold the workload's synthetic context, pooled with
+    rotated indexer keys.  The roofline object prices the whole step's
+    algorithmic bytes (weights, selected K/V, pooled keys) against HBM."""
+    import torch
+    from block_sparse_attention_keys_amd import qsa, runner, workloads
+    cfg = BLOCK_BENCH[name]
+    sp = workloads.SPECS[cfg["spec"]]
+    dev = torch.device("cuda:0")
+    case = workloads.make_case(cfg["spec"], seed=0)
+    B, r, k = sp.n_seqs, sp.block_size, sp.k_blocks
+    Hq, Hkv, D, HI, dI = sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads, sp.idx_dim
+    dm, T = cfg["d_model"], sp.n_seqs
+    n_in = workloads.block_n_in(sp)
+    w_bytes = (n_in * dm + dm * Hq * D) * 2
+    kv = idx = 0
+    for c in case.ctx:
+        n = c + 1
+        nb = n // r
+        kv += (r * min(k, nb) + (n - r * nb)) * Hkv * D * 2 * 2
+        idx += nb * dI * 4
+    per_step = w_bytes + kv + idx + T * dm * 2 * 2
+    L = args.layers or max(2, math.ceil(3 * 256e6 / per_step))
+    total = args.warmup + args.steps
+    per_layer_steps = math.ceil(total / L) + 1
+    dc = runner.DeviceCase(case, device=dev, n_layers=L, extra_steps=per_layer_steps,
+                           idx_rope=(cfg["idx_rope_dim"], cfg["rope_theta"]))
+    bp = qsa.make_block_params(dm, cfg["rotary_dim"], cfg["rope_theta"], 1e-6)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+    bf = torch.bfloat16
+
+    def nrm(shape, scale):
+        return (torch.randn(shape, generator=gen, device=dev) * scale).to(bf)
+
+    weights = [{"w_in": nrm((n_in, dm), dm ** -0.5), "w_o": nrm((dm, Hq * D), (Hq * D) ** -0.5),
+                "qn": nrm((D,), 0.1), "kn": nrm((D,), 0.1)} for _ in range(L)]
+    xs = [nrm((T, dm), 1.0) for _ in range(total)]
+    batches = [dc.batch_for([c + j for c in case.ctx], [1] * B) for j in range(per_layer_steps)]
+    ws_bytes = max(qsa.qsa_block_workspace_size(dc.params, bp, bt) for bt in batches)
+    ws = torch.zeros((ws_bytes,), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((T, dm), dtype=bf, device=dev) for _ in range(total)]
+    sels = [torch.empty((T, k), dtype=torch.int32, device=dev) for _ in range(total)]
+    nbls = [torch.empty((T,), dtype=torch.int32, device=dev) for _ in range(total)]
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def fwd(s):
+        l, j = s % L, s // L
+        st, w = dc.layers[l], weights[l]
+        qsa.qsa_block_forward(dc.params, bp, batches[j], xs[s], w["w_in"], w["qn"], w["kn"],
+                              w["w_o"], st["k"], st["v"], st["kI"], st["pooled"], ys[s], sels[s],
+                              nbls[s], ws, sh)
+
+    for s in range(args.warmup):
+        fwd(s)
+    torch.cuda.synchronize(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(args.warmup, total):
+        fwd(s)
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    ms_step = e0.elapsed_time(e1) / args.steps
+    gbps = per_step / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": (f"synthetic (seeded; contexts U[{sp.ctx_lo},{sp.ctx_hi}]; hidden states "
+                 "N(0,1), Linear weights N(0,1/fan_in), all drawn on the GPU)"),
+        "config": {"workload": name, "batch": B, "d_model": dm, "n_q_heads": Hq,
+                   "n_kv_heads": Hkv, "head_dim": D, "block_size": r, "budget": sp.budget,
+                   "idx_heads": HI, "idx_dim": dI, "rotary_dim": cfg["rotary_dim"],
+                   "idx_rope_dim": cfg["idx_rope_dim"], "ctx_min": min(case.ctx),
+                   "ctx_max": max(case.ctx), "paged": True, "layer_copies": L},
+        "step_bytes": {"weights": w_bytes, "selected_kv": kv, "pooled_keys": idx,
+                       "x_y": T * dm * 4},
+        "roofline": {"bound": "hbm", "kernel": "whole block step (qsa_block_forward)",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(ms_step * 1e3, 2),
+                     "bytes_per_launch": per_step, "traffic": None},
+    }
     print(json.dumps(res), flush=True)
 
 

@@ -545,8 +545,9 @@ qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* b
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int T = batch->n_tokens;
   float* p1 = reinterpret_cast<float*>(ws_at(ws, bl.off_p1));
-  QSA_TRY(hip_status(qsa::launch_proj_gemm(x, w_in, p1, T, bl.n_in, bl.d_model, bl.S1, st),
-                     "input projection launch"));
+  QSA_TRY(hip_status(
+      qsa::launch_proj_gemm(x, w_in, p1, nullptr, T, bl.n_in, bl.d_model, bl.S1, st),
+      "input projection launch"));
   qsa::BlockPrepArgs a;
   a.part = p1;
   a.S = bl.S1;
@@ -573,8 +574,9 @@ qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* b
                          k_idx_cache, pooled, attn, sel_opt, n_blocks_opt,
                          ws_at(ws, bl.off_core), st));
   float* p2 = reinterpret_cast<float*>(ws_at(ws, bl.off_p2));
-  QSA_TRY(hip_status(qsa::launch_proj_gemm(attn, w_o, p2, T, bl.d_model, bl.hqd, bl.S2, st),
+  QSA_TRY(hip_status(qsa::launch_proj_gemm(attn, w_o, p2, y, T, bl.d_model, bl.hqd, bl.S2, st),
                      "output projection launch"));
+  if (bl.S2 == 1) return QSA_OK;  // the GEMM wrote y
   return hip_status(qsa::launch_proj_reduce(p2, bl.S2, (int64_t)T * bl.d_model, y, st),
                     "output reduce launch");
 }

@@ -44,7 +44,8 @@ constexpr uint32_t kGemmOob = 0x80000000u;
 
 __global__ __launch_bounds__(256) void proj_gemm_kernel(const uint16_t* __restrict__ A,
                                                         const uint16_t* __restrict__ B,
-                                                        float* __restrict__ part, int M, int N,
+                                                        float* __restrict__ part,
+                                                        uint16_t* __restrict__ out, int M, int N,
                                                         int K, int k_split) {
   __shared__ float red[4][32][33];
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -106,21 +107,32 @@ __global__ __launch_bounds__(256) void proj_gemm_kernel(const uint16_t* __restri
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wid][16 * i + 4 * q4 + r][16 * j + c16] = acc[i][j][r];
   __syncthreads();
-  // Sum the four waves (in wave order) and store this split's partial tile.
+  // Sum the four waves (in wave order) and store this split's partial tile,
+  // or (out given: one split) the bf16 result.
   float* P = part + (int64_t)s * M * N;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int idx = threadIdx.x + 256 * e, rr = idx >> 5, cc = idx & 31;
     const int m = m0 + rr, n = n0 + cc;
     const float v = ((red[0][rr][cc] + red[1][rr][cc]) + red[2][rr][cc]) + red[3][rr][cc];
-    if (m < M && n < N) P[(int64_t)m * N + n] = v;
+    if (m < M && n < N) {
+      if (out != nullptr) out[(int64_t)m * N + n] = bf16_rne(v);
+      else P[(int64_t)m * N + n] = v;
+    }
   }
 }
 
-// Sum of the S partials of element (m, n), splits in order.
+// Sum of the S (<= kMaxSplits) partials of element idx, splits in order; all
+// loads are issued before the first add (unconditional, at clamped splits).
+constexpr int kMaxSplits = 16;
 __device__ __forceinline__ float sum_parts(const float* part, int S, int64_t MN, int64_t idx) {
+  float p[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) p[s] = part[min(s, S - 1) * MN + idx];
   float v = 0.0f;
-  for (int s = 0; s < S; ++s) v += part[s * MN + idx];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) v += p[s];
   return v;
 }
 
@@ -147,12 +159,13 @@ __device__ QueryPosB token_pos(const Geo& g, int t) {
   return {p, p >= 0 && p < g.cap};
 }
 
-// One workgroup per token.  Rows of the stacked input projection, one wave
-// per row at a time: q heads, gate heads, k heads, v heads, indexer-query
-// heads, the indexer key.  Lane l holds values l and l + 64 of a row.
+// Grid (token, group of 4 rows); one wave per row of the stacked input
+// projection: q heads, gate heads, k heads, v heads, indexer-query heads,
+// the indexer key.  Lane l holds values l and l + 64 of a row.
 __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a) {
   __shared__ float rowbuf[4][128];
   const int t = blockIdx.x, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (g.r > 0 && blockIdx.y == 0 && threadIdx.x < g.HI) a.w[(int64_t)t * g.HI + threadIdx.x] = 1.0f;
   const QueryPosB qp = token_pos(g, t);
   const int64_t pos = qp.ok ? qp.p : 0;
   const int D = g.D, Hq = g.Hq, Hkv = g.Hkv, HI = g.HI, dI = g.dI;
@@ -160,7 +173,8 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
   const int64_t MN = (int64_t)g.T * a.n_in;
   const float* P = a.part + (int64_t)t * a.n_in;
   float* row = rowbuf[wid];
-  for (int rw = wid; rw < n_rows; rw += 4) {
+  const int rw = blockIdx.y * 4 + wid;
+  if (rw < n_rows) {
     int kind, head, base, len;  // kind: 0 q, 1 gate, 2 k, 3 v, 4 indexer q, 5 indexer k
     if (rw < Hq) { kind = 0; head = rw; base = head * D; len = D; }
     else if (rw < 2 * Hq) { kind = 1; head = rw - Hq; base = (Hq + head) * D; len = D; }
@@ -205,7 +219,6 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
                   : kind == 4 ? rope_at(row, x, R, g.idx_freq, pos)
                               : rope_at(row, x, R, a.freq, pos);
         }
-        wave_sync();  // the row is read before the next one is written
         v[0] = rv[0];
         v[1] = rv[1];
       }
@@ -225,27 +238,27 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
       if (x < len) dst[x] = bf16_rne(v[e]);
     }
   }
-  if (g.r > 0 && threadIdx.x < HI) a.w[(int64_t)t * HI + threadIdx.x] = 1.0f;
 }
 
 }  // namespace
 
 int gemm_splits(int M, int N, int K) {
   const int64_t tiles = (int64_t)((M + 31) / 32) * ((N + 31) / 32);
-  int64_t S = (768 + tiles - 1) / tiles;
-  S = std::max<int64_t>(1, std::min<int64_t>(S, K / 128));
+  int64_t S = (384 + tiles - 1) / tiles;
+  S = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(S, K / 128), kMaxSplits));
   const int64_t ks = ((K + S - 1) / S + 127) / 128 * 128;
   return (int)((K + ks - 1) / ks);
 }
 
 int gemm_k_split(int K, int S) { return (int)(((K + S - 1) / S + 127) / 128 * 128); }
 
-hipError_t launch_proj_gemm(const void* A, const void* B, float* part, int M, int N, int K, int S,
-                            hipStream_t st) {
+hipError_t launch_proj_gemm(const void* A, const void* B, float* part, void* out_bf16, int M,
+                            int N, int K, int S, hipStream_t st) {
   const int ks = gemm_k_split(K, S);
   dim3 grid((N + 31) / 32, (M + 31) / 32, S);
-  proj_gemm_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A),
-                                         static_cast<const uint16_t*>(B), part, M, N, K, ks);
+  proj_gemm_kernel<<<grid, 256, 0, st>>>(
+      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), part,
+      S == 1 ? static_cast<uint16_t*>(out_bf16) : nullptr, M, N, K, ks);
   return hipGetLastError();
 }
 
@@ -256,7 +269,8 @@ hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, h
 }
 
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st) {
-  block_prep_kernel<<<g.T, 256, 0, st>>>(g, a);
+  const int n_rows = 2 * g.Hq + 2 * g.Hkv + (g.r > 0 ? g.HI + 1 : 0);
+  block_prep_kernel<<<dim3(g.T, (n_rows + 3) / 4), 256, 0, st>>>(g, a);
   return hipGetLastError();
 }
 

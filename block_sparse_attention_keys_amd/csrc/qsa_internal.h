@@ -102,8 +102,10 @@ struct BlockPrepArgs {
 // Split count and k range per split of a projection GEMM of M x N x K.
 int gemm_splits(int M, int N, int K);
 int gemm_k_split(int K, int S);
-hipError_t launch_proj_gemm(const void* A, const void* B, float* part, int M, int N, int K, int S,
-                            hipStream_t st);
+// part: [S][M][N] fp32 partials; with S == 1 and out_bf16 given, the result
+// goes straight to out_bf16 [M][N] instead.
+hipError_t launch_proj_gemm(const void* A, const void* B, float* part, void* out_bf16, int M,
+                            int N, int K, int S, hipStream_t st);
 hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, hipStream_t st);
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st);
 

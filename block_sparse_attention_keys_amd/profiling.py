@@ -23,12 +23,18 @@ import statistics
 from typing import Dict, List
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(PKG, "csrc", "qsa_kernels.hip")
+CSRC = os.path.join(PKG, "csrc")
 
 
 def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over every source file of the library (kernels, shared device
+    helpers, launch configuration), in name order."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def _one(pattern: str) -> str:
