@@ -41,6 +41,7 @@ constexpr int kMaxK = qsa::kPlanMaxK;
 
 struct Plan {
   qsa::Geo geo;
+  qsa::RopeTab idx_rope;  // pooled-key rotary frequencies
   qsa::AttnPlan attn;
   int elem;
   size_t off_scores, off_sel, off_nblk, off_part, total;
@@ -153,14 +154,15 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   g.pooled_ld = r ? (int32_t)round_up((b.kv_capacity + r - 1) / r, 64) : 0;
   g.nbcap = r ? b.max_kv_len / r : 0;
   const double a_scale = p.attn_scale > 0.0f ? (double)p.attn_scale : 1.0 / sqrt((double)g.D);
+  // Rotary indexer keys: frequencies theta^(-2i/R) in fp64 on the host.
+  g.idx_rope_dim = p.idx_rope_dim;
+  for (int i = 0; i < 64; ++i)
+    out->idx_rope.f[i] = i < p.idx_rope_dim / 2
+                        ? pow((double)p.idx_rope_theta, -2.0 * (double)i / (double)p.idx_rope_dim)
+                        : 0.0;
   // 8-bit K/V: the K scale joins the softmax scale, and the rotated basis
   // multiplies every score by D (H H = D I); the V scale and the 1/D of the
   // un-rotation are applied to the output.
-  g.idx_rope_dim = p.idx_rope_dim;
-  for (int i = 0; i < 64; ++i)
-    g.idx_freq[i] = i < p.idx_rope_dim / 2
-                        ? pow((double)p.idx_rope_theta, -2.0 * (double)i / (double)p.idx_rope_dim)
-                        : 0.0;
   g.kv8 = p.kv_dtype == QSA_KV_FP8 ? 1 : 0;
   g.rot = g.kv8 && p.kv_rotate ? 1 : 0;
   g.inv_k_scale = g.kv8 ? 1.0f / p.k_scale : 1.0f;
@@ -281,7 +283,7 @@ qsa_status qsa_store_kv(const qsa_params* params, const qsa_batch* batch, const 
   QSA_TRY(need(k_cache, "k_cache", 16));
   QSA_TRY(need(v_cache, "v_cache", 16));
   return hip_status(qsa::launch_append_pool(pl.geo, pl.elem, k_new, v_new, nullptr, k_cache,
-                                            v_cache, nullptr, nullptr,
+                                            v_cache, nullptr, nullptr, pl.idx_rope,
                                             static_cast<hipStream_t>(stream)),
                     "store launch");
 }
@@ -298,7 +300,7 @@ qsa_status qsa_pool_keys(const qsa_params* params, const qsa_batch* batch,
   QSA_TRY(need(k_idx_cache, "k_idx_cache", 16));
   QSA_TRY(need(pooled, "pooled", 16));
   return hip_status(qsa::launch_append_pool(pl.geo, pl.elem, nullptr, nullptr, k_idx_new,
-                                            nullptr, nullptr, k_idx_cache, pooled,
+                                            nullptr, nullptr, k_idx_cache, pooled, pl.idx_rope,
                                             static_cast<hipStream_t>(stream)),
                     "qsa_pool_keys launch");
 }
@@ -404,13 +406,13 @@ qsa_status forward_launch(const Plan& pl, const qsa_batch* batch, const void* q,
     float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
     const qsa::AppendArgs ap = {k_new, v_new, k_idx_new, k_cache, v_cache, k_idx_cache};
     QSA_TRY(hip_status(
-        qsa::launch_score_append(pl.geo, pl.elem, q_idx, w, pooled, scores, ap, st),
+        qsa::launch_score_append(pl.geo, pl.elem, q_idx, w, pooled, scores, ap, pl.idx_rope, st),
         "append/score launch"));
   } else {
     QSA_TRY(hip_status(qsa::launch_append_pool(pl.geo, pl.elem, k_new, v_new,
                                                qsa_layer ? k_idx_new : nullptr, k_cache, v_cache,
                                                qsa_layer ? k_idx_cache : nullptr,
-                                               qsa_layer ? pooled : nullptr, st),
+                                               qsa_layer ? pooled : nullptr, pl.idx_rope, st),
                        "append/pool launch"));
     if (qsa_layer) {
       float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
@@ -554,6 +556,7 @@ qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* b
   a.n_in = bl.n_in;
   a.eps = block->norm_eps;
   a.rotary_dim = block->rotary_dim;
+  for (int i = 0; i < 64; ++i) a.idx_freq[i] = bl.core.idx_rope.f[i];
   for (int i = 0; i < 64; ++i)
     a.freq[i] = i < block->rotary_dim / 2
                     ? pow((double)block->rope_theta, -2.0 * (double)i / (double)block->rotary_dim)

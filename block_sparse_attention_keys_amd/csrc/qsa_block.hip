@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
           const int x = lane + 64 * e;
           // (one call per table: no pointer chosen at run time)
           rv[e] = x >= len ? 0.0f
-                  : kind == 4 ? rope_at(row, x, R, g.idx_freq, pos)
+                  : kind == 4 ? rope_at(row, x, R, a.idx_freq, pos)
                               : rope_at(row, x, R, a.freq, pos);
         }
         v[0] = rv[0];

@@ -28,11 +28,17 @@ struct Geo {
   float inv_k_scale, inv_v_scale;  // 8-bit: 1 / scale, the factor applied before encoding
   float out_scale;             // 8-bit: V scale (and 1/D when rotated) on the attention output
   int32_t idx_rope_dim;        // > 0: each pooled key's first idx_rope_dim values are rotated
-                               // at its block's first position
-  double idx_freq[64];         // their rotary frequencies theta^(-2i/idx_rope_dim), fp64
+                               // at its block's first position (frequencies: RopeTab)
   const int32_t* cu_q;
   const int32_t* past_len;
   const int32_t* page_table;
+};
+
+// Rotary frequencies theta^(-2i/R), fp64, computed on the host.  Kept out of
+// Geo and passed only to the kernels that rotate: a 512-byte table inside
+// Geo costs every kernel scalar registers.
+struct RopeTab {
+  double f[64];
 };
 
 // Split-KV plan of the attention kernels.
@@ -53,7 +59,7 @@ enum ElemType { kF32 = 0, kBF16 = 1 };
 // Launchers; each returns hipGetLastError() after its launches.
 hipError_t launch_append_pool(const Geo& g, int elem, const void* k_new, const void* v_new,
                               const void* kI_new, void* k_cache, void* v_cache, void* kI_cache,
-                              float* pooled, hipStream_t st);
+                              float* pooled, const RopeTab& idx_rope, hipStream_t st);
 hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w, float* pooled,
                         float* scores, hipStream_t st);
 // Rows a decode-form score launch appends (at most one new token per sequence).
@@ -67,7 +73,7 @@ struct AppendArgs {
 };
 hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const float* w,
                                float* pooled, float* scores, const AppendArgs& ap,
-                               hipStream_t st);
+                               const RopeTab& idx_rope, hipStream_t st);
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
                          hipStream_t st);
 // In-kernel selection (decode attention): scores in, selections out (either
@@ -89,6 +95,7 @@ struct BlockPrepArgs {
   float eps;                   // RMSNorm epsilon
   int32_t rotary_dim;          // rotated values of each q / k head (rotate-half)
   double freq[64];             // their frequencies theta^(-2i/rotary_dim), fp64
+  double idx_freq[64];         // the indexer query's (qsa_params idx_rope_dim / theta)
   const uint16_t* q_norm;      // [D] bf16, applied as (1 + w)
   const uint16_t* k_norm;
   uint16_t* q;                 // [T][Hq][D] bf16 outputs

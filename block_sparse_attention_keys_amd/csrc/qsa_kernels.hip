@@ -186,7 +186,7 @@ template <typename E>
 __global__ __launch_bounds__(256) void append_pool_kernel(
     Geo g, const E* __restrict__ k_new, const E* __restrict__ v_new,
     const E* __restrict__ kI_new, E* __restrict__ k_cache, E* __restrict__ v_cache,
-    E* __restrict__ kI_cache, float* __restrict__ pooled) {
+    E* __restrict__ kI_cache, float* __restrict__ pooled, RopeTab rt) {
   const int t = blockIdx.x, tid = threadIdx.x;
   const QueryPos qp = query_pos(g, t);
   if (!qp.ok) return;
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
     __shared__ float mrow[128];
     if (tid < dI) mrow[tid] = mean;
     __syncthreads();
-    if (tid < dI) mean = rope_at(mrow, tid, g.idx_rope_dim, g.idx_freq, (int64_t)j << g.log2r);
+    if (tid < dI) mean = rope_at(mrow, tid, g.idx_rope_dim, rt.f, (int64_t)j << g.log2r);
   }
   if (tid < dI) pooled[((int64_t)qp.b * dI + tid) * g.pooled_ld + j] = mean;
 }
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(64) void score_kernel(
     Geo g, const E* __restrict__ qI, const float* __restrict__ w, float* __restrict__ pooled,
     float* __restrict__ scores, const E* __restrict__ k_new, const E* __restrict__ v_new,
     const E* __restrict__ kI_new, E* __restrict__ k_cache, E* __restrict__ v_cache,
-    E* __restrict__ kI_cache) {
+    E* __restrict__ kI_cache, RopeTab rt) {
   constexpr bool APPEND = MODE != 0, ONEQ = MODE == 2;
   constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
   __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
@@ -442,7 +442,7 @@ __global__ __launch_bounds__(64) void score_kernel(
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int x = min(lane + 64 * c, DI - 1);
-        rv[c] = rope_at(newpool, x, g.idx_rope_dim, g.idx_freq, (int64_t)s0);
+        rv[c] = rope_at(newpool, x, g.idx_rope_dim, rt.f, (int64_t)s0);
       }
       wave_sync();
 #pragma unroll
@@ -1884,7 +1884,7 @@ hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const voi
 
 template <typename E, int DI, int MODE>
 void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
-              const AppendArgs& ap, hipStream_t st) {
+              const AppendArgs& ap, const RopeTab& rt, hipStream_t st) {
   // (decode form: two more workgroups per token, the appender and the pooler)
   dim3 grid(g.T, std::max(1, (g.nbcap + 63) / 64) + (MODE != 0 ? 2 : 0));
   const E* q = static_cast<const E*>(qI);
@@ -1895,20 +1895,20 @@ void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float
   E* vc = static_cast<E*>(ap.v_cache);
   E* ic = static_cast<E*>(ap.kI_cache);
   if (g.HI <= 4) {
-    score_kernel<E, 4, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
+    score_kernel<E, 4, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic, rt);
   } else if (g.HI <= 8) {
-    score_kernel<E, 8, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
+    score_kernel<E, 8, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic, rt);
   } else {
-    score_kernel<E, 16, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic);
+    score_kernel<E, 16, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic, rt);
   }
 }
 
 template <typename E, int MODE>
 hipError_t score_h(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
-                   const AppendArgs& ap, hipStream_t st) {
-  if (g.dI == 32) score_hd<E, 32, MODE>(g, qI, w, pooled, scores, ap, st);
-  else if (g.dI == 64) score_hd<E, 64, MODE>(g, qI, w, pooled, scores, ap, st);
-  else score_hd<E, 128, MODE>(g, qI, w, pooled, scores, ap, st);
+                   const AppendArgs& ap, const RopeTab& rt, hipStream_t st) {
+  if (g.dI == 32) score_hd<E, 32, MODE>(g, qI, w, pooled, scores, ap, rt, st);
+  else if (g.dI == 64) score_hd<E, 64, MODE>(g, qI, w, pooled, scores, ap, rt, st);
+  else score_hd<E, 128, MODE>(g, qI, w, pooled, scores, ap, rt, st);
   return hipGetLastError();
 }
 
@@ -1920,18 +1920,18 @@ bool attend_supported(int G, int D) {
 
 hipError_t launch_append_pool(const Geo& g, int elem, const void* k_new, const void* v_new,
                               const void* kI_new, void* k_cache, void* v_cache, void* kI_cache,
-                              float* pooled, hipStream_t st) {
+                              float* pooled, const RopeTab& idx_rope, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   if (elem == kBF16) {
     append_pool_kernel<uint16_t><<<g.T, 256, 0, st>>>(
         g, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
         static_cast<const uint16_t*>(kI_new), static_cast<uint16_t*>(k_cache),
-        static_cast<uint16_t*>(v_cache), static_cast<uint16_t*>(kI_cache), pooled);
+        static_cast<uint16_t*>(v_cache), static_cast<uint16_t*>(kI_cache), pooled, idx_rope);
   } else {
     append_pool_kernel<float><<<g.T, 256, 0, st>>>(
         g, static_cast<const float*>(k_new), static_cast<const float*>(v_new),
         static_cast<const float*>(kI_new), static_cast<float*>(k_cache),
-        static_cast<float*>(v_cache), static_cast<float*>(kI_cache), pooled);
+        static_cast<float*>(v_cache), static_cast<float*>(kI_cache), pooled, idx_rope);
   }
   return hipGetLastError();
 }
@@ -1940,19 +1940,20 @@ hipError_t launch_score(const Geo& g, int elem, const void* qI, const float* w, 
                         float* scores, hipStream_t st) {
   if (g.T == 0 || g.nbcap == 0) return hipSuccess;
   const AppendArgs none = {};
-  return elem == kBF16 ? score_h<uint16_t, 0>(g, qI, w, pooled, scores, none, st)
-                       : score_h<float, 0>(g, qI, w, pooled, scores, none, st);
+  const RopeTab no_rope = {};
+  return elem == kBF16 ? score_h<uint16_t, 0>(g, qI, w, pooled, scores, none, no_rope, st)
+                       : score_h<float, 0>(g, qI, w, pooled, scores, none, no_rope, st);
 }
 
 hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const float* w,
                                float* pooled, float* scores, const AppendArgs& ap,
-                               hipStream_t st) {
+                               const RopeTab& idx_rope, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   if (g.one_q)
-    return elem == kBF16 ? score_h<uint16_t, 2>(g, qI, w, pooled, scores, ap, st)
-                         : score_h<float, 2>(g, qI, w, pooled, scores, ap, st);
-  return elem == kBF16 ? score_h<uint16_t, 1>(g, qI, w, pooled, scores, ap, st)
-                       : score_h<float, 1>(g, qI, w, pooled, scores, ap, st);
+    return elem == kBF16 ? score_h<uint16_t, 2>(g, qI, w, pooled, scores, ap, idx_rope, st)
+                         : score_h<float, 2>(g, qI, w, pooled, scores, ap, idx_rope, st);
+  return elem == kBF16 ? score_h<uint16_t, 1>(g, qI, w, pooled, scores, ap, idx_rope, st)
+                       : score_h<float, 1>(g, qI, w, pooled, scores, ap, idx_rope, st);
 }
 
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
