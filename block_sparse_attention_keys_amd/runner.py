@@ -235,15 +235,24 @@ class BlockDeviceCase:
     workload on one GPU; every call goes through qsa_block_forward.  The
     context is filled by the block's own prefill calls."""
 
-    def __init__(self, bc, device="cuda", layout: str = "paged", page_size: int = 64):
+    def __init__(self, bc, device="cuda", layout: str = "paged", page_size: int = 64,
+                 kv_fp8: bool = False, kv_rotate: bool = False):
         sp = bc.spec
         self.bc, self.spec, self.device = bc, sp, torch.device(device)
         B = sp.n_seqs
         self.B, self.r = B, sp.block_size
+        self.kv8, self.kv_rotate = kv_fp8, bool(kv_fp8 and kv_rotate)
+        # (the block's k and v are RMS-normed / unit-variance: the rotated
+        # values' scale follows as for the workload draws, times sqrt(D))
+        sd = (1.0 if self.kv_rotate else sp.head_dim ** -0.5) * sp.head_dim ** 0.5
+        self.k_scale = self.v_scale = float(np.float32(8.0 * sd / 448.0)) if kv_fp8 else 1.0
         self.params = qsa.make_params(sp.n_q_heads, sp.n_kv_heads, sp.head_dim, sp.n_idx_heads,
                                       sp.idx_dim, sp.block_size, sp.budget, qsa.QSA_BF16,
                                       idx_rope_dim=bc.idx_rope_dim,
-                                      idx_rope_theta=bc.idx_rope_theta)
+                                      idx_rope_theta=bc.idx_rope_theta,
+                                      kv_dtype=qsa.QSA_KV_FP8 if kv_fp8 else qsa.QSA_KV_SAME,
+                                      kv_rotate=int(self.kv_rotate), k_scale=self.k_scale,
+                                      v_scale=self.v_scale)
         self.block = qsa.make_block_params(bc.d_model, bc.rotary_dim, bc.rope_theta, bc.norm_eps)
         Hkv, D, dI = sp.n_kv_heads, sp.head_dim, sp.idx_dim
         n_tok = bc.n_tok
@@ -269,8 +278,9 @@ class BlockDeviceCase:
             self.page_table = None
             kv_shape, ki_shape = (B, Hkv, self.cap, D), (B, self.cap, dI)
         bf = torch.bfloat16
-        self.st = {"k": torch.zeros(kv_shape, dtype=bf, device=self.device),
-                   "v": torch.zeros(kv_shape, dtype=bf, device=self.device)}
+        kv_dt = torch.uint8 if kv_fp8 else bf
+        self.st = {"k": torch.zeros(kv_shape, dtype=kv_dt, device=self.device),
+                   "v": torch.zeros(kv_shape, dtype=kv_dt, device=self.device)}
         if self.r > 0:
             self.st["kI"] = torch.zeros(ki_shape, dtype=bf, device=self.device)
             ld = qsa.qsa_pooled_ld(self.params, self.batch_for([0] * B, [1] * B))

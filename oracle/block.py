@@ -122,11 +122,13 @@ def core_dims(bd: dict) -> dict:
 
 
 def block(orc, bd: dict, x, W_in, qn_w, kn_w, W_o, q_pos, want_scores: bool = False,
-          nb_cap: Optional[int] = None) -> dict:
+          nb_cap: Optional[int] = None, kv8: Optional[tuple] = None) -> dict:
     """The QSA block for the queries at positions q_pos of ONE sequence whose
     tokens 0..n-1 have hidden states x [n][d_model] (the caches hold all of
     them).  Returns y [nq][d_model] (fp32), the selections, and the
-    intermediate bf16-valued tensors of the queries."""
+    intermediate bf16-valued tensors of the queries.  kv8 = (rotate,
+    k_scale, v_scale): the K/V cache holds 8-bit codes of the block's k and
+    v (the oracle's own encoding, qsa_oracle_kv8_encode)."""
     x = widen(x)
     n = x.shape[0]
     q_pos = np.asarray(q_pos, np.int64)
@@ -135,8 +137,16 @@ def block(orc, bd: dict, x, W_in, qn_w, kn_w, W_o, q_pos, want_scores: bool = Fa
     nq = q_pos.size
     HI = bd["n_idx_heads"]
     w = np.ones((nq, max(HI, 1)), np.float32) if bd["block_size"] > 0 else None
-    ref = orc.sequence(core_dims(bd), kv["k"], kv["v"], kv["kI"], q_pos, qs["q"], qs["qI"], w,
-                       qs["gate"], want_scores=want_scores, nb_cap=nb_cap)
+    if kv8 is None:
+        ref = orc.sequence(core_dims(bd), kv["k"], kv["v"], kv["kI"], q_pos, qs["q"], qs["qI"], w,
+                           qs["gate"], want_scores=want_scores, nb_cap=nb_cap)
+    else:
+        rotate, ks, vs = kv8
+        inv = lambda sc: float(np.float32(1.0) / np.float32(sc))  # noqa: E731
+        Kc = orc.kv8_encode(kv["k"], rotate, inv(ks))
+        Vc = orc.kv8_encode(kv["v"], rotate, inv(vs))
+        ref = orc.sequence_kv8(core_dims(bd), Kc, Vc, rotate, ks, vs, kv["kI"], q_pos, qs["q"],
+                               qs["qI"], w, qs["gate"], want_scores=want_scores, nb_cap=nb_cap)
     attn = bf16_round(ref["out"]).reshape(nq, -1)
     ref["attn"] = attn
     ref["y"] = project(attn, W_o)

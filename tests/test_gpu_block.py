@@ -68,8 +68,8 @@ def test_rotated_pooled_keys_chunked_prefill():
     assert np.array_equal(pooled_rows(dc)[0, :ref.shape[0]], ref)
 
 
-def _run_block(bc, layout="paged", keep=None):
-    dc = runner.BlockDeviceCase(bc, layout=layout)
+def _run_block(bc, layout="paged", keep=None, **kw):
+    dc = runner.BlockDeviceCase(bc, layout=layout, **kw)
     res = {}
     for i in range(len(bc.calls)):
         c = dc.call_inputs(i)
@@ -82,7 +82,7 @@ def _run_block(bc, layout="paged", keep=None):
     return dc, res
 
 
-def _check_block(bc, result, sample=None, seed=0):
+def _check_block(bc, result, sample=None, seed=0, kv8=None):
     orc = oracle.load()
     y, sel, nblk, spans = result
     dims = bc.dims()
@@ -99,7 +99,7 @@ def _check_block(bc, result, sample=None, seed=0):
         if sample is not None and n_q > sample:
             idx = np.sort(rng.choice(n_q, size=sample, replace=False))
         ref = oblock.block(orc, dims, bc.x[b][:e], bc.w_in, bc.q_norm, bc.k_norm, bc.w_o, s + idx,
-                           want_scores=r > 0)
+                           want_scores=r > 0, kv8=kv8)
         same = np.ones(len(idx), bool)
         if r > 0:
             k = ref["sel"].shape[1]
@@ -157,3 +157,14 @@ def test_block_dense_layer():
     _, res = _run_block(bc)
     for i in sorted(res):
         _check_block(bc, res[i], sample=48, seed=i)
+
+
+def test_block_with_rotated_8bit_cache():
+    """The block over an 8-bit K/V cache in the Hadamard basis: the block's
+    bf16 k and v rows are rotated, scaled and encoded on append."""
+    bc = workloads.make_block_case("ragged_paged_decode_128k_bf16", d_model=512, n_seqs=3,
+                                   ctx_range=(900, 4000), chunk=2048, decode_steps=2)
+    dc, res = _run_block(bc, kv_fp8=True, kv_rotate=True)
+    kv8 = (True, dc.k_scale, dc.v_scale)
+    for i in sorted(res):
+        _check_block(bc, res[i], sample=64, seed=i, kv8=kv8)
