@@ -37,6 +37,18 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
+def measured_sha256(run_dir: str) -> str:
+    """The library sources' sha256 recorded next to a measurement
+    (``source_sha256.txt`` in the run directory or its parent, written by
+    ``python -m block_sparse_attention_keys_amd.profiling sha > FILE`` on the
+    GPU machine before profiling); the current sources' when none was recorded."""
+    for d in (run_dir, os.path.dirname(os.path.normpath(run_dir))):
+        f = os.path.join(d, "source_sha256.txt")
+        if os.path.exists(f):
+            return open(f).read().strip()
+    return kernel_source_sha256()
+
+
 def _one(pattern: str) -> str:
     files = sorted(glob.glob(pattern, recursive=True))
     if not files:
@@ -94,7 +106,7 @@ def counter_per_launch(d: str, counter: str, kernel_regex: str) -> Dict[str, flo
 def cmd_trace(a) -> None:
     rows = trace_summary(a.dir)
     lines = [f"# {a.title}", "", f"command: {a.cmd}",
-             f"kernel_source_sha256: {kernel_source_sha256()}", "",
+             f"kernel_source_sha256: {measured_sha256(a.dir)}", "",
              "| kernel | calls | avg us | min us | max us | total ms |",
              "|---|---|---|---|---|---|"]
     for r in rows:
@@ -124,7 +136,7 @@ def cmd_counters(a) -> None:
     traffic = fk * 1024.0 * f_factor + wk * 1024.0 * w_factor
     lines = [f"# {a.title}", "", f"command (fetch): {a.cmd_fetch}", f"command (write): {a.cmd_write}",
              f"command (copy calibration): {a.cmd_copy}",
-             f"kernel: {a.kernel}", f"kernel_source_sha256: {kernel_source_sha256()}",
+             f"kernel: {a.kernel}", f"kernel_source_sha256: {measured_sha256(a.fetch)}",
              "fetch_kib_per_dispatch_by_kernel: " +
              ", ".join(f"{k} {v:.1f}" for k, v in fetch.items()),
              "write_kib_per_dispatch_by_kernel: " +
@@ -155,6 +167,29 @@ def read_summary(path: str) -> Dict[str, str]:
     return out
 
 
+def cmd_pmc(a) -> None:
+    """Mean per dispatch of every counter in a --pmc run, for the kernels
+    matching --kernel."""
+    path = _one(os.path.join(a.dir, "**", "*counter_collection.csv"))
+    per: Dict[tuple, List[float]] = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if re.search(a.kernel, r["Kernel_Name"]):
+                per.setdefault((_short(r["Kernel_Name"]), r["Counter_Name"]), []).append(
+                    float(r["Counter_Value"]))
+    lines = [f"# {a.title}", "", f"command: {a.cmd}",
+             f"kernel_source_sha256: {measured_sha256(a.dir)}", "",
+             "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
+    for (k, c), v in sorted(per.items()):
+        lines.append(f"| {k} | {c} | {len(v)} | {statistics.mean(v):.6g} |")
+    if a.note:
+        lines += ["", a.note]
+    text = "\n".join(lines) + "\n"
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -165,6 +200,11 @@ def main() -> None:
     t.add_argument("--out", required=True)
     t.add_argument("--only", default="")
     t.add_argument("--note", default="")
+    sub.add_parser("sha")
+    q = sub.add_parser("pmc")
+    for k in ("dir", "cmd", "title", "out", "kernel"):
+        q.add_argument("--" + k, required=True)
+    q.add_argument("--note", default="")
     c = sub.add_parser("counters")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         c.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -178,7 +218,10 @@ def main() -> None:
     c.add_argument("--title", required=True)
     c.add_argument("--out", required=True)
     a = ap.parse_args()
-    (cmd_trace if a.what == "trace" else cmd_counters)(a)
+    if a.what == "sha":
+        print(kernel_source_sha256())
+        return
+    {"trace": cmd_trace, "counters": cmd_counters, "pmc": cmd_pmc}[a.what](a)
 
 
 if __name__ == "__main__":
