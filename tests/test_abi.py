@@ -197,6 +197,14 @@ def test_block_params_rejected(L, kw, bkw, status, needle):
     assert qsa.qsa_block_workspace_size(p, bp, Bt()) == 0
 
 
+def test_block_zero_tokens_is_a_noop(L):
+    p, bp = P(), qsa.make_block_params(512, 64, 1e6)
+    b = Bt(n_tokens=0, cu_q=None, past_len=None)
+    assert qsa.qsa_block_workspace_size(p, bp, b) == 0
+    assert L.qsa_block_forward(C.byref(p), C.byref(bp), C.byref(b), *([None] * 13), 0,
+                               None) == qsa.QSA_OK
+
+
 def test_block_workspace_and_pointers(L):
     p, bp = P(idx_rope_dim=64, idx_rope_theta=1e6), qsa.make_block_params(512, 64, 1e6)
     need = qsa.qsa_block_workspace_size(p, bp, Bt())
