@@ -68,6 +68,31 @@ def test_rotated_pooled_keys_chunked_prefill():
     assert np.array_equal(pooled_rows(dc)[0, :ref.shape[0]], ref)
 
 
+def test_rotated_pooled_keys_verify_and_fp32():
+    """Rotated pooled keys through the general decode form (several new
+    tokens per sequence per call) and through the fp32 kernels."""
+    orc = oracle.load()
+    case = workloads.make_case("spec_verify_ragged_bf16", n_seqs=3, ctx_range=(2000, 5000),
+                               steps=20)
+    dc = runner.DeviceCase(case, idx_rope=ROPE)
+    res = run_calls(dc, keep={0, 19})
+    seqf = SeqF32(case)
+    for i in sorted(res):
+        check_call(dc, seqf, res[i])
+    got = pooled_rows(dc)
+    for b in range(case.spec.n_seqs):
+        ref = _oracle_pooled(orc, case.kI[b], 64, *ROPE)
+        assert np.array_equal(got[b, :ref.shape[0]], ref), f"pooled keys of seq {b}"
+    case = workloads.make_case("tiny_prefill_f32", chunk=96)
+    dc = runner.DeviceCase(case, layout="paged", idx_rope=(16, 1e4))
+    res = run_calls(dc)
+    seqf = SeqF32(case)
+    for i in sorted(res):
+        check_call(dc, seqf, res[i])
+    ref = _oracle_pooled(orc, case.kI[0], 16, 16, 1e4)
+    assert np.array_equal(pooled_rows(dc)[0, :ref.shape[0]], ref)
+
+
 def _run_block(bc, layout="paged", keep=None, **kw):
     dc = runner.BlockDeviceCase(bc, layout=layout, **kw)
     res = {}
