@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
 // contiguous bytes); each lane holds all d_I values of its block's pooled key
 // in registers, loaded together.
 // MODE 0: scoring only (the pooled cache is complete).
-// MODE 1, 2: the decode form, where every sequence has at most one new token,
+// MODE 1: the decode form, where every sequence has at most one new token,
 // so no token of the call needs a row that another token appends.  Two more
 // workgroups per token (grid y = 0, 1: dispatched first, so that their loads
 // are not queued behind the scorers') do the rest of the step off the
@@ -285,9 +285,10 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
 // token completes a block, pools that block (the new row from kI_new, the
 // older rows from the cache, summed in token order as in append_pool_kernel),
 // stores it in the pooled cache and writes its score (the scorers skip it).
-// MODE 2: every sequence has exactly one new token (token t is sequence t's),
-// so the scorers read the pooled keys before the position is known as well:
-// one memory round trip.
+// The scorers request a sequence's pooled keys only once its position shows
+// that their group holds candidates: a batch's shorter sequences read no
+// columns past their own blocks (requesting the keys before the position is
+// known saves no time and reads up to the longest context for every token).
 
 // Score of one pooled key held in LDS (pk[x], x < DI), computed by lane h < HI
 // for head h, then summed over heads by lane 0 in head order: the same fmaf
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(64) void score_kernel(
     float* __restrict__ scores, const E* __restrict__ k_new, const E* __restrict__ v_new,
     const E* __restrict__ kI_new, E* __restrict__ k_cache, E* __restrict__ v_cache,
     E* __restrict__ kI_cache, RopeTab rt) {
-  constexpr bool APPEND = MODE != 0, ONEQ = MODE == 2;
+  constexpr bool APPEND = MODE != 0;
   constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
   __shared__ __attribute__((aligned(16))) float qT[DI * HIM];  // [x][h]
   __shared__ float wsh[HIM];
@@ -473,12 +474,9 @@ __global__ __launch_bounds__(64) void score_kernel(
       pk[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                             rs, col, (uint32_t)(x * g.pooled_ld * 4), 0));
   };
-  if constexpr (ONEQ) load_keys(t);
   const QueryPos qp = query_pos(g, t);
   const int nb = qp.ok ? ((qp.p + 1) >> g.log2r) : 0;
-  if constexpr (!ONEQ) {
-    if (group * 64 < nb) load_keys(qp.b);
-  }
+  if (group * 64 < nb) load_keys(qp.b);
   // (decode form) the block this token completes is scored by the pooler
   const int jnew = (APPEND && qp.ok && ((qp.p + 1) & (g.r - 1)) == 0) ? nb - 1 : -1;
   __syncthreads();
@@ -1949,9 +1947,6 @@ hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const flo
                                float* pooled, float* scores, const AppendArgs& ap,
                                const RopeTab& idx_rope, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  if (g.one_q)
-    return elem == kBF16 ? score_h<uint16_t, 2>(g, qI, w, pooled, scores, ap, idx_rope, st)
-                         : score_h<float, 2>(g, qI, w, pooled, scores, ap, idx_rope, st);
   return elem == kBF16 ? score_h<uint16_t, 1>(g, qI, w, pooled, scores, ap, idx_rope, st)
                        : score_h<float, 1>(g, qI, w, pooled, scores, ap, idx_rope, st);
 }
