@@ -88,6 +88,8 @@ def main():
     name = args.workload
     if name in BLOCK_BENCH:
         return bench_block(args, name)
+    if name == "block_chunked_prefill_32k":
+        return bench_block_prefill(args, name)
     sp = workloads.SPECS[name]
     if sp.kind != "decode":
         return bench_prefill(args, name)
@@ -319,6 +321,59 @@ def bench_block(args, name):
                      "bytes_per_launch": per_step, "traffic": None},
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_block_prefill(args, name):
+    """The QSA block over the 32K chunked prefill (d_model 2560): a step is
+    every 4096-token chunk through qsa_block_forward, caches filled by the
+    block itself.  The roofline prices the step's projection flops plus the
+    selected-block attention flops against the bf16 MFMA peak."""
+    import torch
+    from block_sparse_attention_keys_amd import runner, workloads
+    bc = workloads.make_block_case("chunked_prefill_32k_bf16", d_model=2560, chunk=4096,
+                                   decode_steps=0)
+    sp = bc.spec
+    dc = runner.BlockDeviceCase(bc)
+    calls = [dc.call_inputs(i) for i in range(len(bc.calls))]
+    T = sum(c["T"] for c in calls)
+    n_in = workloads.block_n_in(sp)
+    proj = 2.0 * T * bc.d_model * (n_in + sp.n_q_heads * sp.head_dim)
+    r, k = sp.block_size, sp.k_blocks
+    n = np.arange(1, sp.prefill_len + 1)
+    nb = n // r
+    attn = float((r * np.minimum(k, nb) + (n - r * nb)).sum()) * sp.n_q_heads * 4 * sp.head_dim
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for c in calls:
+            dc.forward(c)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = (proj + attn) / (ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; hidden states N(0,1), Linear weights N(0,1/fan_in))",
+        "config": {"workload": name, "tokens": T, "chunk": 4096, "d_model": bc.d_model,
+                   "n_q_heads": sp.n_q_heads, "n_kv_heads": sp.n_kv_heads,
+                   "head_dim": sp.head_dim, "block_size": r, "budget": sp.budget},
+        "gflop_per_step": {"projections": round(proj / 1e9, 1), "selected_attention": round(attn / 1e9, 1)},
+        "roofline": {"bound": "mfma", "kernel": "whole block step (qsa_block_forward per chunk)",
+                     "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "avg_launch_us": round(ms * 1e3 / len(calls), 1),
+                     "flops_per_launch": round((proj + attn) / len(calls)), "traffic": None},
+    }), flush=True)
 
 
 def counter_traffic(summary_name):

@@ -122,6 +122,97 @@ __global__ __launch_bounds__(256) void proj_gemm_kernel(const uint16_t* __restri
   }
 }
 
+// The product for many rows (prefill): a workgroup computes a 128 x 128 tile
+// through LDS.  Per k-step of 32, the 256 threads bring the A and B tiles
+// (128 rows x 64 bytes each, 16 bytes per thread and load, two loads each)
+// into LDS rows padded to 40 elements (80 bytes: the 16 rows a fragment read
+// touches fall on distinct banks), double-buffered, the next step's loads in
+// flight while the current step multiplies.  Wave (wm, wn) owns the 64 x 64
+// quarter at rows 64 wm, columns 64 wn: per k-step 4 A and 4 B fragments
+// from LDS and 16 MFMAs.
+constexpr int kTile = 128, kLdsRow = 40;
+
+__global__ __launch_bounds__(256) void proj_gemm_tiled_kernel(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ B,
+                                                              float* __restrict__ part,
+                                                              uint16_t* __restrict__ out, int M,
+                                                              int N, int K) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][kTile * kLdsRow];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kTile * kLdsRow];
+  const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+  const int c16 = lane & 15, q4 = lane >> 4, wm = wid >> 1, wn = wid & 1;
+  const int m0 = blockIdx.y * kTile, n0 = blockIdx.x * kTile;
+  const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A, (uint32_t)((int64_t)M * K * 2));
+  const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(B, (uint32_t)((int64_t)N * K * 2));
+  // This thread's two 16-byte pieces of each tile: rows tid/4 and tid/4 + 64,
+  // bytes 16 (tid % 4) of the row's 64-byte k-step.
+  const int lr = tid >> 2, lc = tid & 3;
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int m = m0 + lr + 64 * h, n = n0 + lr + 64 * h;
+    aoff[h] = m < M ? (uint32_t)(m * K + 8 * lc) * 2u : kGemmOob;
+    boff[h] = n < N ? (uint32_t)(n * K + 8 * lc) * 2u : kGemmOob;
+  }
+  uint4 ga[2], gb[2];
+  auto fetch = [&](int kt) {
+    const uint32_t kbyte = (uint32_t)kt * 64u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ga[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ars, aoff[h] + kbyte, 0, 0));
+      gb[h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[h] + kbyte, 0, 0));
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<uint4*>(&As[buf][(lr + 64 * h) * kLdsRow + 8 * lc]) = ga[h];
+      *reinterpret_cast<uint4*>(&Bs[buf][(lr + 64 * h) * kLdsRow + 8 * lc]) = gb[h];
+    }
+  };
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int KT = K >> 5;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) fetch(kt + 1);
+    uint4 af[4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = *reinterpret_cast<const uint4*>(&As[buf][(64 * wm + 16 * i + c16) * kLdsRow + 8 * q4]);
+      bfr[i] = *reinterpret_cast<const uint4*>(&Bs[buf][(64 * wn + 16 * i + c16) * kLdsRow + 8 * q4]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                            __builtin_bit_cast(bf16x8_t, bfr[j]),
+                                                            acc[i][j], 0, 0, 0);
+    if (kt + 1 < KT) stash(buf ^ 1);
+    __syncthreads();
+  }
+  // C fragment: row 16 i + 4 q4 + r, column 16 j + c16 of the wave's quarter.
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 64 * wm + 16 * i + 4 * q4 + r, n = n0 + 64 * wn + 16 * j + c16;
+        if (m < M && n < N) {
+          if (out != nullptr) out[(int64_t)m * N + n] = bf16_rne(acc[i][j][r]);
+          else part[(int64_t)m * N + n] = acc[i][j][r];
+        }
+      }
+}
+
 // Sum of the S (<= kMaxSplits) partials of element idx, splits in order; all
 // loads are issued before the first add (unconditional, at clamped splits).
 constexpr int kMaxSplits = 16;
@@ -242,7 +333,13 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
 
 }  // namespace
 
+// Many rows (and enough 128 x 128 tiles to fill the chip): the LDS-tiled kernel.
+static bool gemm_tiled(int M, int N) {
+  return M >= 256 && (int64_t)((M + kTile - 1) / kTile) * ((N + kTile - 1) / kTile) >= 256;
+}
+
 int gemm_splits(int M, int N, int K) {
+  if (gemm_tiled(M, N)) return 1;
   const int64_t tiles = (int64_t)((M + 31) / 32) * ((N + 31) / 32);
   int64_t S = (384 + tiles - 1) / tiles;
   S = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(S, K / 128), kMaxSplits));
@@ -255,10 +352,17 @@ int gemm_k_split(int K, int S) { return (int)(((K + S - 1) / S + 127) / 128 * 12
 hipError_t launch_proj_gemm(const void* A, const void* B, float* part, void* out_bf16, int M,
                             int N, int K, int S, hipStream_t st) {
   const int ks = gemm_k_split(K, S);
+  uint16_t* out = S == 1 ? static_cast<uint16_t*>(out_bf16) : nullptr;
+  if (gemm_tiled(M, N) && S == 1) {
+    dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
+    proj_gemm_tiled_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A),
+                                                 static_cast<const uint16_t*>(B), part, out, M, N,
+                                                 K);
+    return hipGetLastError();
+  }
   dim3 grid((N + 31) / 32, (M + 31) / 32, S);
-  proj_gemm_kernel<<<grid, 256, 0, st>>>(
-      static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), part,
-      S == 1 ? static_cast<uint16_t*>(out_bf16) : nullptr, M, N, K, ks);
+  proj_gemm_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A),
+                                         static_cast<const uint16_t*>(B), part, out, M, N, K, ks);
   return hipGetLastError();
 }
 
