@@ -15,10 +15,12 @@
 //               waves take interleaved k-steps of the workgroup's k range and
 //               are summed through LDS; the grid splits K further into fp32
 //               partials when the tiles alone cannot fill the chip (decode).
-//   block_prep  one workgroup per token: sums the partials of the stacked
-//               input projection, RMSNorm (1 + w) and RoPE on the q and k
-//               heads, RoPE on the indexer query heads, bf16 rounding of
-//               everything the QSA path reads; head weights all ones.
+//   proj_gemm_tiled  the same product for many rows (prefill): 128 x 128
+//               workgroup tiles staged through LDS, double-buffered.
+//   block_prep  one wave per (token, projection row): sums the partials of
+//               the stacked input projection, RMSNorm (1 + w) and RoPE on the
+//               q and k heads, RoPE on the indexer query heads, bf16 rounding
+//               of everything the QSA path reads; head weights all ones.
 //   proj_reduce sums the partials of o_proj into the bf16 output.
 #include <hip/hip_runtime.h>
 #include <math.h>
