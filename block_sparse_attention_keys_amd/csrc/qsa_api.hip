@@ -1,6 +1,7 @@
 // C ABI of the QSA hot path: argument validation, workspace layout and launch
 // sequencing.  No arithmetic of the method happens here; every step runs in
-// the kernels of qsa_kernels.hip.
+// the kernels of qsa_kernels.hip and qsa_block.hip.  (The host fills only the
+// rotary frequency tables, theta^(-2i/R) in fp64 with the C library's pow.)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>

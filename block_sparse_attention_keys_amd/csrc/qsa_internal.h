@@ -1,5 +1,6 @@
 // Internal interface between the C-ABI host layer (qsa_api.hip) and the
-// gfx950 kernels (qsa_kernels.hip).  Not installed; not part of the ABI.
+// gfx950 kernels (qsa_kernels.hip, qsa_block.hip).  Not installed; not part of
+// the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
