@@ -18,6 +18,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqsa.so")
+# debug build for tests: counts the K/V rows the attention kernels load
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
+PROBE_FLAGS = ["-DQSA_COUNT_KEYS"]
 SOURCES = ["qsa_api.hip", "qsa_kernels.hip", "qsa_block.hip"]
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -35,7 +38,7 @@ def _hipcc() -> str:
 def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     """Compile every source to an object (in parallel), then link ``out``."""
     hipcc = _hipcc()
-    bdir = os.path.join(PKG, "_build")
+    bdir = os.path.join(PKG, "_build", "probe" if extra else "lib")
     os.makedirs(bdir, exist_ok=True)
 
     def comp(src):
@@ -59,5 +62,10 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list:
+    """The product library and the probe build."""
+    return [build(LIB, verbose=verbose), build(PROBE_LIB, PROBE_FLAGS, verbose=verbose)]
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_all(verbose="-v" in sys.argv))

@@ -585,5 +585,14 @@ qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* b
                     "output reduce launch");
 }
 
+#ifdef QSA_COUNT_KEYS
+// Debug builds only (include/qsa_probe.h).
+int64_t qsa_probe_keys_visited(int32_t reset) {
+  unsigned long long v = 0;
+  if (qsa::keys_visited(&v, reset != 0) != hipSuccess) return -1;
+  return (int64_t)v;
+}
+#endif
+
 }  // extern "C"
 

@@ -117,6 +117,12 @@ hipError_t launch_proj_gemm(const void* A, const void* B, float* part, void* out
 hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, hipStream_t st);
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st);
 
+#ifdef QSA_COUNT_KEYS
+// Debug builds: the device counter of K/V rows the attention kernels loaded
+// (synchronous copies; reset sets it to zero after reading).
+hipError_t keys_visited(unsigned long long* value, bool reset);
+#endif
+
 // True when a kernel instantiation exists for G heads per KV head and dim D.
 bool attend_supported(int G, int D);
 

@@ -31,6 +31,22 @@ namespace {
 
 #include "qsa_device.h"
 
+// Debug builds only (QSA_COUNT_KEYS): every attention kernel adds the number
+// of valid K/V rows it loads, per (token, KV head), to one device counter.
+#ifdef QSA_COUNT_KEYS
+__device__ unsigned long long g_keys_visited;
+// Lane 0 of the calling wave adds the wave's count of set predicates.
+#define QSA_COUNT_ROWS(pred)                                                              \
+  do {                                                                                    \
+    const unsigned long long n_ = __popcll(__ballot(pred));                               \
+    if ((threadIdx.x & 63) == 0 && n_) atomicAdd(&g_keys_visited, n_);                    \
+  } while (0)
+#else
+#define QSA_COUNT_ROWS(pred) \
+  do {                       \
+  } while (0)
+#endif
+
 
 
 
@@ -980,6 +996,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
         const int s = list_token(g, L, srow, i);
         if (s >= 0 && s <= qp.p) row = kv_row(g, qp.b, kvh, s);
       }
+      QSA_COUNT_ROWS(row >= 0);
       float z[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) z[h] = 0.0f;
@@ -1415,6 +1432,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         const int nit = it + 64 * kWaves;
         const bool has_next = nit < r1;
         const int32_t* rows = rowidx + (it - r0);
+        QSA_COUNT_ROWS(rows[lane] >= 0);
         const bool full = __all(rows[lane] >= 0);
 
         uint4 qb[4];
@@ -1679,6 +1697,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
     const int r1 = min(r0 + RND, L.n_list);
     for (int it = r0; it < r1; it += 64) {
       const int32_t* tr = rows + (it - r0);
+      QSA_COUNT_ROWS(it + lane < r1 && tr[lane] >= 0);
       // K as the B operand: key tile n, k-step ks -> 16 B of row (16n + c16).
       uint4 kb[4][4];
       int32_t krow[4];
@@ -1911,6 +1930,15 @@ hipError_t score_h(const Geo& g, const void* qI, const float* w, float* pooled, 
 }
 
 }  // namespace
+
+#ifdef QSA_COUNT_KEYS
+hipError_t keys_visited(unsigned long long* value, bool reset) {
+  hipError_t e = hipMemcpyFromSymbol(value, HIP_SYMBOL(g_keys_visited), sizeof(*value));
+  if (e != hipSuccess || !reset) return e;
+  const unsigned long long zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_keys_visited), &zero, sizeof(zero));
+}
+#endif
 
 bool attend_supported(int G, int D) {
   return (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) && (D == 64 || D == 128);

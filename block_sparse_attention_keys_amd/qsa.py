@@ -8,6 +8,7 @@ A missing library raises immediately: there is no fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes as C
 import os
 from typing import Optional
@@ -65,6 +66,11 @@ def lib(path: str = LIB_PATH) -> C.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = _load(path)
+    return _lib
+
+
+def _load(path: str) -> C.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m block_sparse_attention_keys_amd.build`")
@@ -92,8 +98,28 @@ def lib(path: str = LIB_PATH) -> C.CDLL:
     L.qsa_block_workspace_size.argtypes = [P, BP, B]
     L.qsa_block_forward.restype = C.c_int
     L.qsa_block_forward.argtypes = [P, BP, B] + [vp] * 13 + [C.c_size_t, vp]
-    _lib = L
+    if hasattr(L, "qsa_probe_keys_visited"):
+        L.qsa_probe_keys_visited.restype = C.c_int64
+        L.qsa_probe_keys_visited.argtypes = [C.c_int32]
     return L
+
+
+PROBE_PATH = os.path.join(PKG, "libqsa_probe.so")
+
+
+@contextlib.contextmanager
+def probe_library(path: str = PROBE_PATH):
+    """Route every call of this module through the debug build (include/
+    qsa_probe.h) for the duration of the block; yields the loaded library,
+    whose qsa_probe_keys_visited reads the rows-loaded counter."""
+    global _lib
+    saved = _lib
+    P = _load(path)
+    _lib = P
+    try:
+        yield P
+    finally:
+        _lib = saved
 
 
 def _ptr(x) -> Optional[int]:

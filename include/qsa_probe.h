@@ -1,0 +1,29 @@
+/* Test probe of the QSA library: present only in the debug build
+ * libqsa_probe.so (compiled with QSA_COUNT_KEYS), never in libqsa.so.
+ *
+ * The gather, not a mask (llama.cpp PR #27739 page, LocalAI QSA-block
+ * commit, section "What the context length buys": the block reads
+ * keys_visited = n_sel rows per query and KV head, not the dense prefix):
+ * every attention kernel of the probe build adds the number of valid K/V
+ * rows it loads to one device counter.  After a call, the counter equals the
+ * sum over the call's (query token, KV head) units of the token set size
+ * r * min(k, nb) + tail (every visible row for a dense layer). */
+#ifndef QSA_PROBE_H
+#define QSA_PROBE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The counter's value (after all work on the device has finished: the read
+ * is a synchronous copy); reset != 0 sets it to zero afterwards.  -1 on a
+ * HIP error. */
+int64_t qsa_probe_keys_visited(int32_t reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_PROBE_H */

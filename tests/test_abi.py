@@ -236,3 +236,23 @@ def test_workspace_grows_with_batch(L):
     big = qsa.qsa_workspace_size(P(), Bt(n_tokens=64, max_q_len=64, max_kv_len=4096,
                                          kv_capacity=4096))
     assert big > small > 0
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "qsa_probe.h")
+
+
+def test_probe_symbols_only_in_the_probe_build(L):
+    """include/qsa_probe.h: the row counter exists in libqsa_probe.so only;
+    the probe build exports the whole boundary as well."""
+    if not os.path.exists(qsa.PROBE_PATH):
+        from block_sparse_attention_keys_amd import build
+        build.build(build.PROBE_LIB, build.PROBE_FLAGS)
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    probe_names = sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
+    assert probe_names == ["qsa_probe_keys_visited"]
+    P = C.CDLL(qsa.PROBE_PATH)
+    for n in probe_names:
+        assert hasattr(P, n), n
+        assert not hasattr(L, n), f"{n} leaked into the product library"
+    for n in declared_functions():
+        assert hasattr(P, n), n
