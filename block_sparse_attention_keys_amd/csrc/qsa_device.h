@@ -39,6 +39,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
+// 16 bytes from lane src_byte / 4 (ds_bpermute: a lane permutation through
+// the LDS crossbar, no LDS storage).
+__device__ __forceinline__ uint4 lane_gather(uint4 v, int src_byte) {
+  return make_uint4((uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.x),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.y),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.z),
+                    (uint32_t)__builtin_amdgcn_ds_bpermute(src_byte, (int)v.w));
+}
+
 constexpr uint32_t kOobOffset = 0xFFFFF000u;  // past the end of every buffer that uses it
 constexpr int kStreamPolicy = 2;              // non-temporal: each K/V row is read once
 

@@ -1634,8 +1634,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 //   V -> LDS transposed [dim][key] (4 keys packed per 8-byte store), read as
 //                  the B operand: O[head][dim] += P x V, 8 dim tiles x 2 k-steps.
 // LDS rows are padded to 136 B, which keeps the 16-lane B reads conflict-free.
+// A tile's K and V rows are all requested before its first MFMA (one memory
+// round trip per tile).
 template <int G>
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
+__global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
@@ -1698,17 +1700,48 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
     for (int it = r0; it < r1; it += 64) {
       const int32_t* tr = rows + (it - r0);
       QSA_COUNT_ROWS(it + lane < r1 && tr[lane] >= 0);
-      // K as the B operand: key tile n, k-step ks -> 16 B of row (16n + c16).
-      uint4 kb[4][4];
-      int32_t krow[4];
+      // Loads are coalesced: the 4 lanes of a quad read 64 contiguous bytes
+      // of one row (lane / 4: row, lane % 4: 16-byte chunk), so a load
+      // instruction touches 16 row segments, not 64 scattered 16-byte pieces.
+      // K: load n, k-step ks holds row 16n + kq, bytes 16 cq + 64 ks; it is
+      // then passed across lanes to the B-operand layout (key 16n + c16, dims
+      // 32 ks + 8 grp ..).  V: rows 4 kq + s, chunks cq + 4 j (8 dims each),
+      // transposed through LDS below.
+      const int kq = lane >> 2, cq = lane & 3;
+      int32_t krow[4], klr[4], vrow[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
         krow[n] = tr[16 * n + c16];
-        const int64_t base = (int64_t)(krow[n] >= 0 ? krow[n] : 0) * D + 8 * grp;
+        klr[n] = tr[16 * n + kq];
+      }
+#pragma unroll
+      for (int sft = 0; sft < 4; ++sft) vrow[sft] = tr[4 * kq + sft];
+      uint4 kl[4][4], vv[4][4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int64_t base = (int64_t)(klr[n] >= 0 ? klr[n] : 0) * D + 8 * cq;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-          kb[n][ks] = *reinterpret_cast<const uint4*>(kc + base + 32 * ks);
+          kl[n][ks] = *reinterpret_cast<const uint4*>(kc + base + 32 * ks);
       }
+#pragma unroll
+      for (int sft = 0; sft < 4; ++sft) {
+        const bool ok = vrow[sft] >= 0;
+        const int64_t base = (int64_t)(ok ? vrow[sft] : 0) * D;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint4 w = *reinterpret_cast<const uint4*>(vc + base + 8 * (cq + 4 * j));
+          vv[j][sft] = ok ? w : make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+      // Lane (c16, grp) takes the chunk that lane 4 c16 + grp loaded.
+      const int src = 4 * (4 * c16 + grp);
+      uint4 kb[4][4];
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kb[n][ks] = lane_gather(kl[n][ks], src);
       // S = Q K^T
       f32x4_t S[4];
 #pragma unroll
@@ -1718,19 +1751,6 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
         for (int ks = 0; ks < 4; ++ks)
           S[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               qa[ks], __builtin_bit_cast(bf16x8_t, kb[n][ks]), S[n], 0, 0, 0);
-      }
-      // V rows 4*c16 + s, chunks grp + 4 j (8 dims each).
-      uint4 vv[4][4];
-#pragma unroll
-      for (int sft = 0; sft < 4; ++sft) {
-        const int32_t rv = tr[4 * c16 + sft];
-        const bool ok = rv >= 0;
-        const int64_t base = (int64_t)(ok ? rv : 0) * D;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint4 w = *reinterpret_cast<const uint4*>(vc + base + 8 * (grp + 4 * j));
-          vv[j][sft] = ok ? w : make_uint4(0u, 0u, 0u, 0u);
-        }
       }
       // Online softmax: lane rows r -> head 4 grp + r; keys 16n + c16.
       float alpha[4];
@@ -1750,11 +1770,12 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
         const float mn = fmaxf(m[r], mx);
         alpha[r] = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - mn);
         m[r] = mn;
+        const float mb = mn == -INFINITY ? 0.0f : mn;  // while mn is -inf, so is every z
         float lsum = 0.0f;
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-          const float z = S[n][r];
-          const uint16_t pb = (z == -INFINITY) ? (uint16_t)0 : bf16_rne(exp2f(z - mn));
+          // exp2(-inf) = 0; hardware round-to-nearest-even to bf16
+          const uint16_t pb = __builtin_bit_cast(uint16_t, (__bf16)exp2f(S[n][r] - mb));
           lsum += to_f32(pb);
           reinterpret_cast<uint16_t*>(Pl + (4 * grp + r) * RS)[16 * n + c16] = pb;
         }
@@ -1765,10 +1786,10 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) O[n][r] *= alpha[r];
       }
-      // V^T -> LDS: for dim 8 c + e, keys 4 c16 .. 4 c16 + 3 as one 8-byte store.
+      // V^T -> LDS: for dim 8 c + e, keys 4 kq .. 4 kq + 3 as one 8-byte store.
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int c = grp + 4 * j;
+        const int c = cq + 4 * j;
         const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[j][0]);
         const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[j][1]);
         const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[j][2]);
@@ -1779,7 +1800,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(
           uint2 pk;
           pk.x = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sl);
           pk.y = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sl);
-          *reinterpret_cast<uint2*>(VT + (8 * c + e) * RS + 8 * c16) = pk;
+          *reinterpret_cast<uint2*>(VT + (8 * c + e) * RS + 8 * kq) = pk;
         }
       }
       wave_sync();
