@@ -1624,36 +1624,42 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 // Matrix-core layout of v_mfma_f32_16x16x32_bf16 (64 lanes, l = lane):
 //   A[i][k]: i = l%16, k = 8*(l/16) + e;  B[k][j]: j = l%16, k = 8*(l/16) + e;
 //   C[i][j]: j = l%16, i = 4*(l/16) + r.
-// Per 64-key tile of the unit's selection list:
-//   S[head][key] = sum over 4 k-steps of Q (A: heads padded to 16 rows, fixed
-//                  per unit, in registers) x K^T (B: 16 B of a cache row per
-//                  lane, straight from memory): 4 key tiles x 4 = 16 MFMAs;
-//   online softmax in base 2 on the accumulator layout (a head's 64 keys sit
-//                  in 16 lanes x 4 tiles: in-lane max, then 4 DPP steps);
-//   P (bf16) -> LDS [head][key], read back as the A operand;
-//   V -> LDS transposed [dim][key] (4 keys packed per 8-byte store), read as
-//                  the B operand: O[head][dim] += P x V, 8 dim tiles x 2 k-steps.
-// LDS rows are padded to 136 B, which keeps the 16-lane B reads conflict-free.
-// A tile's K and V rows are all requested before its first MFMA (one memory
-// round trip per tile).
+// Per 64-key tile of the unit's selection list (lane l = (c16, grp)):
+//   S^T[key][head] = K (A: key 16n + c16) x Q^T (B: head c16, zero past G):
+//       4 key tiles x 4 k-steps = 16 MFMAs; lane (c16, grp) then holds head
+//       c16's scores of keys 16n + 4 grp + r;
+//   online softmax in base 2: a head's 64 scores sit in the 4 lanes c16 + 16 g
+//       (in-lane maximum over 16, then two row swaps);
+//   P feeds P x V as the A operand straight from those registers: k-step ks
+//       takes keys 16 (2 ks) + 4 grp + r, then 16 (2 ks + 1) + 4 grp + r (the
+//       order of the keys inside a tile is free as long as V follows it);
+//   V goes to LDS row-major as loaded; its B operand (dim 16n + c16, the same
+//       8 keys) comes back through two transposing reads (ds_read_b64_tr_b16:
+//       inside a 16-lane group, element j of lane i is element i % 4 of the 8
+//       bytes that lane 4 j + i / 4 addresses);
+//   O[head][dim] += P x V, 8 dim tiles x 2 k-steps; each head's rescale
+//       factor reaches the lanes holding its O rows through ds_bpermute.
+// K and V are loaded coalesced (the 4 lanes of a quad read 64 contiguous
+// bytes of one row) and both requested before the first MFMA; K reaches the
+// A-operand layout through ds_bpermute.  V rows are 288 B apart in LDS, so the
+// 4 rows one 16-lane transposing read touches fall on distinct banks.
 template <int G>
 __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     Geo g, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
     uint16_t* __restrict__ out) {
-  static_assert(G <= 16, "heads per KV head must fit the 16 MFMA rows");
+  static_assert(G <= 16, "heads per KV head must fit the 16 MFMA columns");
   constexpr int D = 128;
-  constexpr int RS = 136;                 // LDS row stride (bytes) of VT and P
+  constexpr int VS = 288;                 // LDS row stride (bytes) of the V tile
   constexpr int RND = 128;                // list positions resolved per round
-  __shared__ __attribute__((aligned(16))) unsigned char VT_all[kWaves][D * RS];
-  __shared__ __attribute__((aligned(16))) unsigned char P_all[kWaves][16 * RS];
-  __shared__ int32_t rows_all[kWaves][RND];
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) unsigned char V_all[kWaves][64 * VS];
+  __shared__ __attribute__((aligned(16))) int32_t rows_all[kWaves][RND];
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int unit = blockIdx.x * kWaves + wid;
   if (unit >= g.T * g.Hkv) return;  // whole wave; only wave-level sync below
-  unsigned char* VT = VT_all[wid];
-  unsigned char* Pl = P_all[wid];
+  unsigned char* Vl = V_all[wid];
   int32_t* rows = rows_all[wid];
   const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
   const QueryPos qp = query_pos(g, t);
@@ -1662,8 +1668,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
   const int32_t* srow = sel + (int64_t)t * g.k;
   const int h0 = kvh * G;
   const int c16 = lane & 15, grp = lane >> 4;
+  const int kq = lane >> 2, cq = lane & 3;  // coalesced loads: row, 16-byte chunk
 
-  // Q as the A operand: row c16 = head (zero past G), k = dims 32 ks + 8 grp + e.
+  // Q^T as the B operand: column c16 = head (zero past G), k = dims 32 ks + 8 grp + e.
   bf16x8_t qa[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
@@ -1672,13 +1679,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
       w = *reinterpret_cast<const uint4*>(q + ((int64_t)t * g.Hq + h0 + c16) * D + 32 * ks + 8 * grp);
     qa[ks] = __builtin_bit_cast(bf16x8_t, w);
   }
-  float m[4], ls[4];
+  float m = -INFINITY;  // head c16: running maximum (base 2)
+  float ls = 0.0f;      // head c16: this lane's share of the denominator
   f32x4_t O[8];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m[r] = -INFINITY;
-    ls[r] = 0.0f;
-  }
 #pragma unroll
   for (int n = 0; n < 8; ++n) O[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
@@ -1700,20 +1703,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
     for (int it = r0; it < r1; it += 64) {
       const int32_t* tr = rows + (it - r0);
       QSA_COUNT_ROWS(it + lane < r1 && tr[lane] >= 0);
-      // Loads are coalesced: the 4 lanes of a quad read 64 contiguous bytes
-      // of one row (lane / 4: row, lane % 4: 16-byte chunk), so a load
-      // instruction touches 16 row segments, not 64 scattered 16-byte pieces.
-      // K: load n, k-step ks holds row 16n + kq, bytes 16 cq + 64 ks; it is
-      // then passed across lanes to the B-operand layout (key 16n + c16, dims
-      // 32 ks + 8 grp ..).  V: rows 4 kq + s, chunks cq + 4 j (8 dims each),
-      // transposed through LDS below.
-      const int kq = lane >> 2, cq = lane & 3;
-      int32_t krow[4], klr[4], vrow[4];
+      // K: load n, k-step ks holds row 16n + kq, bytes 16 cq + 64 ks.
+      // V: rows 4 kq + s, bytes 16 (cq + 4 j).
+      int32_t klr[4], vrow[4];
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        krow[n] = tr[16 * n + c16];
-        klr[n] = tr[16 * n + kq];
-      }
+      for (int n = 0; n < 4; ++n) klr[n] = tr[16 * n + kq];
 #pragma unroll
       for (int sft = 0; sft < 4; ++sft) vrow[sft] = tr[4 * kq + sft];
       uint4 kl[4][4], vv[4][4];
@@ -1734,15 +1728,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
           vv[j][sft] = ok ? w : make_uint4(0u, 0u, 0u, 0u);
         }
       }
-      // Lane (c16, grp) takes the chunk that lane 4 c16 + grp loaded.
+      // V -> LDS as loaded.
+#pragma unroll
+      for (int sft = 0; sft < 4; ++sft)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(Vl + (4 * kq + sft) * VS + 16 * (cq + 4 * j)) = vv[j][sft];
+      // K to the A-operand layout: lane (c16, grp) takes the chunk lane 4 c16 + grp loaded.
       const int src = 4 * (4 * c16 + grp);
-      uint4 kb[4][4];
-#pragma unroll
-      for (int n = 0; n < 4; ++n)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kb[n][ks] = lane_gather(kl[n][ks], src);
-      // S = Q K^T
       f32x4_t S[4];
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
@@ -1750,91 +1743,79 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
           S[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              qa[ks], __builtin_bit_cast(bf16x8_t, kb[n][ks]), S[n], 0, 0, 0);
+              __builtin_bit_cast(bf16x8_t, lane_gather(kl[n][ks], src)), qa[ks], S[n], 0, 0, 0);
       }
-      // Online softmax: lane rows r -> head 4 grp + r; keys 16n + c16.
-      float alpha[4];
+      // Online softmax of head c16 over this lane's keys 16n + 4 grp + r.
+      int4 kv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float mx = -INFINITY;
+      for (int n = 0; n < 4; ++n) kv[n] = *reinterpret_cast<const int4*>(tr + 16 * n + 4 * grp);
+      float mx = -INFINITY;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          const float z = krow[n] >= 0 ? S[n][r] * g.attn_scale_log2 : -INFINITY;
+      for (int n = 0; n < 4; ++n) {
+        const int vr[4] = {kv[n].x, kv[n].y, kv[n].z, kv[n].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float z = vr[r] >= 0 ? S[n][r] * g.attn_scale_log2 : -INFINITY;
           S[n][r] = z;
           mx = fmaxf(mx, z);
         }
-        mx = fmaxf(mx, dpp<0xB1>(mx));
-        mx = fmaxf(mx, dpp<0x4E>(mx));
-        mx = fmaxf(mx, dpp<0x141>(mx));
-        mx = fmaxf(mx, dpp<0x140>(mx));
-        const float mn = fmaxf(m[r], mx);
-        alpha[r] = (m[r] == -INFINITY) ? 0.0f : exp2f(m[r] - mn);
-        m[r] = mn;
-        const float mb = mn == -INFINITY ? 0.0f : mn;  // while mn is -inf, so is every z
-        float lsum = 0.0f;
+      }
+      mx = max_xor32(max_xor16(mx));
+      const float mn = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
+      m = mn;
+      const float mb = mn == -INFINITY ? 0.0f : mn;  // while mn is -inf, so is every z
+      uint32_t pw[4][2];  // bf16 pairs: keys (r 0, 1) and (r 2, 3) of key tile n
+      float lsum = 0.0f;
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
+      for (int n = 0; n < 4; ++n)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
           // exp2(-inf) = 0; hardware round-to-nearest-even to bf16
-          const uint16_t pb = __builtin_bit_cast(uint16_t, (__bf16)exp2f(S[n][r] - mb));
-          lsum += to_f32(pb);
-          reinterpret_cast<uint16_t*>(Pl + (4 * grp + r) * RS)[16 * n + c16] = pb;
+          const uint16_t p0 = __builtin_bit_cast(uint16_t, (__bf16)exp2f(S[n][2 * h] - mb));
+          const uint16_t p1 = __builtin_bit_cast(uint16_t, (__bf16)exp2f(S[n][2 * h + 1] - mb));
+          lsum += to_f32(p0) + to_f32(p1);
+          pw[n][h] = (uint32_t)p0 | ((uint32_t)p1 << 16);
         }
-        ls[r] = fmaf(ls[r], alpha[r], lsum);
+      ls = fmaf(ls, alpha, lsum);
+      // Lane (dim, grp) holds O rows of heads 4 grp + r: their factors.
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float a = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * grp + r), __float_as_int(alpha)));
+#pragma unroll
+        for (int n = 0; n < 8; ++n) O[n][r] *= a;
       }
+      wave_sync();  // the V tile is in LDS
+      // O += P V: k-step ks pairs P's keys 32 ks + 4 grp + (0..3, 16..19)
+      // with two transposing reads of V rows 32 ks + 4 grp + c16 / 4 (+16).
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 pa = make_uint4(pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]);
+        const unsigned char* vrow0 = Vl + (32 * ks + 4 * grp + (c16 >> 2)) * VS + 8 * (c16 & 3);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) O[n][r] *= alpha[r];
-      }
-      // V^T -> LDS: for dim 8 c + e, keys 4 kq .. 4 kq + 3 as one 8-byte store.
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = cq + 4 * j;
-        const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&vv[j][0]);
-        const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&vv[j][1]);
-        const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&vv[j][2]);
-        const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&vv[j][3]);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sl = (e & 1) ? 0x07060302u : 0x05040100u;
-          uint2 pk;
-          pk.x = __builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sl);
-          pk.y = __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sl);
-          *reinterpret_cast<uint2*>(VT + (8 * c + e) * RS + 8 * kq) = pk;
-        }
-      }
-      wave_sync();
-      // O += P V
-      bf16x8_t pa[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        pa[ks] = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(Pl + c16 * RS + 64 * ks + 16 * grp));
-#pragma unroll
-      for (int n = 0; n < 8; ++n) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const uint4 vb =
-              *reinterpret_cast<const uint4*>(VT + (16 * n + c16) * RS + 64 * ks + 16 * grp);
-          O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[ks], __builtin_bit_cast(bf16x8_t, vb),
-                                                         O[n], 0, 0, 0);
+        for (int n = 0; n < 8; ++n) {
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(vrow0 + 32 * n));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(vrow0 + 16 * VS + 32 * n));
+          const uint4 vb = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                      __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+          O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
+                                                         __builtin_bit_cast(bf16x8_t, vb), O[n], 0, 0, 0);
         }
       }
-      wave_sync();
+      wave_sync();  // the next tile may overwrite V
     }
     wave_sync();
   }
-  // Denominators: the 16 lanes of a row group hold partial sums of the same heads.
+  // Denominator of head c16 (its 4 lanes), then to the lanes of its O rows.
+  float l = sum_xor32(sum_xor16(ls));
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    float l = ls[r];
-    l += dpp<0xB1>(l);
-    l += dpp<0x4E>(l);
-    l += dpp<0x141>(l);
-    l += dpp<0x140>(l);
+    const float lr = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * grp + r), __float_as_int(l)));
     const int h = 4 * grp + r;
     if (h >= G) continue;
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const float inv = lr > 0.0f ? 1.0f / lr : 0.0f;
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int64_t idx = ((int64_t)t * g.Hq + h0 + h) * D + 16 * n + c16;
