@@ -1657,11 +1657,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char V_all[kWaves][64 * VS];
   __shared__ __attribute__((aligned(16))) int32_t rows_all[kWaves][RND];
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * kWaves + wid;
-  if (unit >= g.T * g.Hkv) return;  // whole wave; only wave-level sync below
+  int t, kvh;
+  if (8 % g.Hkv == 0) {
+    // Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8):
+    // XCD x serves KV head x / (8 / Hkv), so that its L2 holds the K/V rows of
+    // one head only; consecutive workgroups of an XCD take consecutive tokens.
+    const int per = 8 / g.Hkv, x = blockIdx.x & 7;
+    kvh = x / per;
+    t = ((blockIdx.x >> 3) * per + (x - kvh * per)) * kWaves + wid;
+    if (t >= g.T) return;  // whole wave; only wave-level sync below
+  } else {
+    const int unit = blockIdx.x * kWaves + wid;
+    if (unit >= g.T * g.Hkv) return;
+    t = unit / g.Hkv;
+    kvh = unit - t * g.Hkv;
+  }
   unsigned char* Vl = V_all[wid];
   int32_t* rows = rows_all[wid];
-  const int t = unit / g.Hkv, kvh = unit - t * g.Hkv;
   const QueryPos qp = query_pos(g, t);
   if (!qp.ok) return;
   const ListInfo L = list_info(g, qp, nblk, t);
@@ -1835,7 +1847,11 @@ hipError_t attend_impl(const Geo& g, const AttnPlan& plan, const void* q, const 
   int32_t* nblk_out = fs.n_blocks_out;
   if constexpr (sizeof(E) == 2 && D == 128) {
     if (plan.mfma) {
-      attn_prefill_mfma_kernel<G><<<(g.T * g.Hkv + kWaves - 1) / kWaves, 64 * kWaves, 0, st>>>(
+      // 8 % Hkv == 0: 8 workgroups (one per XCD) per 8 / Hkv groups of kWaves tokens.
+      const int tg = (g.T + kWaves - 1) / kWaves;
+      const int blocks = (8 % g.Hkv == 0) ? 8 * ((tg + 8 / g.Hkv - 1) / (8 / g.Hkv))
+                                          : (g.T * g.Hkv + kWaves - 1) / kWaves;
+      attn_prefill_mfma_kernel<G><<<blocks, 64 * kWaves, 0, st>>>(
           g, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
           static_cast<const uint16_t*>(v_cache), sel, n_blocks,
           static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out));
