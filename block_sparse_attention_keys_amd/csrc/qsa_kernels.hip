@@ -237,32 +237,42 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
   }
   // The token that ends block j pools it.  Rows appended by this same call are
   // read from kI_new (another workgroup may not have stored them yet); older
-  // rows come from the cache.  Thread x < d_I owns column x: it requests 16
-  // rows at a time (a wave reads each row's contiguous bytes) and adds them
-  // in token order, so the sum is the sequential fp32 sum.
+  // rows come from the cache.  The rows are staged in LDS by all threads in
+  // parallel (64 at a time); then one thread per column adds them in token
+  // order, so the sum is the sequential fp32 sum.
   if (pooled == nullptr || g.r == 0 || ((qp.p + 1) & (g.r - 1)) != 0) return;
+  __shared__ float stage[64 * 128];
   const int j = qp.p >> g.log2r;
   const int past = g.past_len[qp.b], t0 = g.cu_q[qp.b];
   const int dI = g.dI;
   float acc = 0.0f;
-  if (tid < dI) {
-    const int s_begin = j << g.log2r;
-    for (int s0 = s_begin; s0 <= qp.p; s0 += 16) {
-      float v[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int s = min(s0 + i, qp.p);
-        if (s >= past) {
-          v[i] = to_f32(kI_new[(int64_t)(t0 + s - past) * dI + tid]);
-        } else {
-          const int64_t row = idx_row(g, qp.b, s);
-          v[i] = row >= 0 ? to_f32(kI_cache[row + tid]) : 0.0f;
-        }
+  for (int s0 = j << g.log2r; s0 <= qp.p; s0 += 64) {
+    const int nrow = min(64, qp.p + 1 - s0);
+    for (int e = tid; e < nrow * dI; e += blockDim.x) {
+      const int rr = e / dI, x = e - rr * dI;
+      const int s = s0 + rr;
+      float v = 0.0f;
+      if (s >= past) {
+        v = to_f32(kI_new[(int64_t)(t0 + s - past) * dI + x]);
+      } else {
+        const int64_t row = idx_row(g, qp.b, s);
+        if (row >= 0) v = to_f32(kI_cache[row + x]);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (s0 + i <= qp.p) acc = acc + v[i];
+      stage[e] = v;
     }
+    __syncthreads();
+    if (tid < dI) {
+      // (16 rows read at a time so the LDS reads overlap; adds in token order)
+      for (int r0 = 0; r0 < nrow; r0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = stage[min(r0 + i, nrow - 1) * dI + tid];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (r0 + i < nrow) acc = acc + v[i];
+      }
+    }
+    __syncthreads();
   }
   float mean = acc * g.inv_r;
   if (g.idx_rope_dim > 0) {
