@@ -1141,7 +1141,7 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 // token makes the same selection; the workgroup of split 0, KV head 0 stores
 // it in sel / nblk when they are given), instead of being read from sel.
 template <int G, bool BUF, bool SEL, bool KV8>
-__global__ __launch_bounds__(256) void attn_decode_kernel(
+__global__ __launch_bounds__(256, 2) void attn_decode_kernel(
     Geo g, AttnPlan plan, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ nblk, const uint16_t* __restrict__ gate,
@@ -1153,9 +1153,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   constexpr int RR = 1024;       // list positions resolved per round
   constexpr int EPR = RR / 256;  // positions per thread per round
   __shared__ int32_t rowidx[RR];                // cache row index, -1 = masked
-  __shared__ uint32_t PP_all[kWaves][32 * G];   // p as bf16 pairs: [token pair][head]
+  constexpr int VS = 288;                        // LDS row stride (bytes) of the V half tile
   __shared__ uint4 qs[16][17];                  // query: [head, padded to 16][16-byte chunk]
-  __shared__ __attribute__((aligned(16))) float wo_all[kWaves][G * D];
+  // One region, two lives: each wave's V half tile (32 rows) during the tile
+  // loop, then the waves' O rows for the merge (after a workgroup barrier).
+  constexpr int kVH = 32 * VS, kWo = G * D * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char tiles[kWaves * (kVH > kWo ? kVH : kWo)];
+  float (*wo_all)[G * D] = reinterpret_cast<float (*)[G * D]>(tiles);
   __shared__ float wm[kWaves][G], wl[kWaves][G];
 
   // Splits run in reverse launch order: the splits that hold an extra tile
@@ -1165,7 +1169,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int c16 = lane & 15, q4 = lane >> 4;    // MFMA column, lane row group
   const int half = lane >> 5, c32 = lane & 31;  // PV: token half, 4-dim chunk
-  uint32_t* PP = PP_all[wid];
+  unsigned char* VH = tiles + wid * kVH;
   const int t = unit / g.Hkv, kvh = unit - t * g.Hkv, h0 = kvh * G;
   const int32_t* srow = sel + (int64_t)t * g.k;
   const int i0 = split_begin(plan, split), i_end = split_begin(plan, split + 1);
@@ -1335,11 +1339,10 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
   const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(kc, kv_bytes), vrs = buffer_rsrc(vc, kv_bytes);
   float m = -INFINITY, lp = 0.0f;  // this lane's head (c16): running max, partial denominator
-  float o[G][4];
+  // O[head][dim] in the MFMA accumulator layout: O[n][r] = head 4 q4 + r, dim 16 n + c16.
+  f32x4_t O[8];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int d = 0; d < 4; ++d) o[h][d] = 0.0f;
+  for (int n = 0; n < 8; ++n) O[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int r0 = i0; r0 < i1; r0 += RR) {
     __syncthreads();  // the previous round's rows are no longer read
@@ -1398,11 +1401,11 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     };
     auto load_v = [&](int at) {
       const int32_t none = at >= 0 ? 0 : -1;
-      const int32_t* rr = rowidx + (at >= 0 ? at - r0 : 0) + 32 * half;
+      const int32_t* rr = rowidx + (at >= 0 ? at - r0 : 0) + half;
       uint32_t vm = 0u;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        const int32_t rj = rr[j] | none;
+        const int32_t rj = rr[2 * j] | none;  // token 2 j + half
         if constexpr (KV8) {
           if constexpr (BUF) {
             const uint32_t off = rj >= 0 ? (uint32_t)rj * D + 4u * c32 : kOobOffset;
@@ -1478,6 +1481,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         const float alpha = (m == -INFINITY) ? 0.0f : exp2f(m - mn);
         m = mn;
         float psum = 0.0f;
+        uint32_t pw[4][2];  // p as bf16 pairs: tokens 16 gi + 4 q4 + (0, 1) and (2, 3)
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
@@ -1486,61 +1490,70 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
             const uint32_t pa = (a == -INFINITY) ? 0u : bf16_rne(exp2f(a - mn));
             const uint32_t pc = (c == -INFINITY) ? 0u : bf16_rne(exp2f(c - mn));
             psum += bf_lo(pa) + bf_lo(pc);
-            if (c16 < G) PP[(8 * gi + 2 * q4 + pr) * G + c16] = pa | (pc << 16);
+            pw[gi][pr] = pa | (pc << 16);
           }
         lp = fmaf(lp, alpha, psum);
+        // Lane (dim, q4) holds the O rows of heads 4 q4 + r: their factors.
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha), h));
+        for (int r = 0; r < 4; ++r) {
+          const float ah =
+              __int_as_float(__builtin_amdgcn_ds_bpermute(4 * (4 * q4 + r), __float_as_int(alpha)));
 #pragma unroll
-          for (int d = 0; d < 4; ++d) o[h][d] *= ah;
+          for (int n = 0; n < 8; ++n) O[n][r] *= ah;
         }
-        wave_sync();
 
         // The next tile's K is requested only now, after the softmax: fewer
         // requests in flight at once stream faster on this memory system.
         __builtin_amdgcn_sched_barrier(0);
         load_k(has_next ? nit : -1);
         __builtin_amdgcn_sched_barrier(0);
+        // O += P V on the matrix cores, in two phases of 32 tokens.  P is the
+        // A operand straight from the softmax registers: phase ph pairs tokens
+        // 32 ph + 4 q4 + (0..3) and 32 ph + 16 + 4 q4 + (0..3) (the order of the
+        // tokens inside a tile is free as long as V follows it).  V: this lane
+        // holds tokens 2 j + half (dims 4 c32 ..); a phase's 32 rows go to VH
+        // row-major, and the B operand (dim 16 n + c16, the same 8 tokens) comes
+        // back through two transposing reads (ds_read_b64_tr_b16: inside a
+        // 16-lane group, element j of lane i is element i % 4 of the 8 bytes
+        // that lane 4 j + i / 4 addresses).
+        typedef short v4s __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int tp = 0; tp < 16; ++tp) {
-          uint2 va, vb;
-          if constexpr (KV8) {  // 4 codes -> 4 bf16 (exact), masked rows zeroed first
-            uint32_t a8 = v8[2 * tp], b8 = v8[2 * tp + 1];
-            if constexpr (!BUF) {
-              a8 &= ((vmask >> (2 * tp)) & 1u) ? ~0u : 0u;
-              b8 &= ((vmask >> (2 * tp + 1)) & 1u) ? ~0u : 0u;
+        for (int ph = 0; ph < 2; ++ph) {
+#pragma unroll
+          for (int jj = 0; jj < 16; ++jj) {
+            const int j = 16 * ph + jj;
+            uint2 v2;
+            if constexpr (KV8) {  // 4 codes -> 4 bf16 (exact), masked rows zeroed first
+              uint32_t a8 = v8[j];
+              if constexpr (!BUF) a8 &= ((vmask >> j) & 1u) ? ~0u : 0u;
+              v2 = make_uint2(
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a8, 1.0f, false)),
+                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a8, 1.0f, true)));
+            } else {
+              v2 = vr[j];
+              if constexpr (!BUF) {
+                const uint32_t km = ((vmask >> j) & 1u) ? ~0u : 0u;
+                v2.x &= km;
+                v2.y &= km;
+              }
             }
-            va = make_uint2(
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a8, 1.0f, false)),
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(a8, 1.0f, true)));
-            vb = make_uint2(
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b8, 1.0f, false)),
-                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b8, 1.0f, true)));
-          } else {
-            va = vr[2 * tp];
-            vb = vr[2 * tp + 1];
+            *reinterpret_cast<uint2*>(VH + (2 * jj + half) * VS + 8 * c32) = v2;
           }
-          if constexpr (!BUF && !KV8) {
-            const uint32_t ka = ((vmask >> (2 * tp)) & 1u) ? ~0u : 0u;
-            const uint32_t kb = ((vmask >> (2 * tp + 1)) & 1u) ? ~0u : 0u;
-            va.x &= ka;
-            va.y &= ka;
-            vb.x &= kb;
-            vb.y &= kb;
-          }
-          uint32_t vp[4];
-          vp[0] = __builtin_amdgcn_perm(vb.x, va.x, 0x05040100u);
-          vp[1] = __builtin_amdgcn_perm(vb.x, va.x, 0x07060302u);
-          vp[2] = __builtin_amdgcn_perm(vb.y, va.y, 0x05040100u);
-          vp[3] = __builtin_amdgcn_perm(vb.y, va.y, 0x07060302u);
-          const uint32_t* pr = PP + (16 * half + tp) * G;
+          wave_sync();
+          const uint4 pa = make_uint4(pw[2 * ph][0], pw[2 * ph][1], pw[2 * ph + 1][0], pw[2 * ph + 1][1]);
+          const unsigned char* v0 = VH + (4 * q4 + (c16 >> 2)) * VS + 8 * (c16 & 3);
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
-            const uint32_t pw = pr[h];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) o[h][d] = dot2_bf16(pw, vp[d], o[h][d]);
+          for (int n = 0; n < 8; ++n) {
+            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(v0 + 32 * n));
+            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s*)(v0 + 16 * VS + 32 * n));
+            const uint4 vb = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                        __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+            O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
+                                                           __builtin_bit_cast(bf16x8_t, vb), O[n], 0, 0, 0);
           }
+          wave_sync();  // VH is rewritten by the next phase or tile
         }
         __builtin_amdgcn_sched_barrier(0);
         load_v(has_next ? nit : -1);
@@ -1552,21 +1565,21 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     }
   }
 
-  // Wave totals: l over the four lane rows of a head, o over the two token halves.
+  // Wave totals: l over the four lane rows of a head; O rows per head (once
+  // every wave is past its tile loop: the rows overlay the V tiles).
   const float lt = sum_xor32(sum_xor16(lp));
+  __syncthreads();
   if (lane < G) {
     wm[wid][lane] = m;
     wl[wid][lane] = lt;
   }
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * q4 + r;
+    if (h < G) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) o[h][d] = sum_xor32(o[h][d]);
-  if (half == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-      *reinterpret_cast<float4*>(&wo_all[wid][h * D + 4 * c32]) =
-          make_float4(o[h][0], o[h][1], o[h][2], o[h][3]);
+      for (int n = 0; n < 8; ++n) wo_all[wid][h * D + 16 * n + c16] = O[n][r];
+    }
   }
   __syncthreads();
 
