@@ -1482,13 +1482,14 @@ __global__ __launch_bounds__(256, 2) void attn_decode_kernel(
         m = mn;
         float psum = 0.0f;
         uint32_t pw[4][2];  // p as bf16 pairs: tokens 16 gi + 4 q4 + (0, 1) and (2, 3)
+        const float mb = mn == -INFINITY ? 0.0f : mn;  // while mn is -inf, so is every z
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi)
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr) {
-            const float a = z[gi][2 * pr], c = z[gi][2 * pr + 1];
-            const uint32_t pa = (a == -INFINITY) ? 0u : bf16_rne(exp2f(a - mn));
-            const uint32_t pc = (c == -INFINITY) ? 0u : bf16_rne(exp2f(c - mn));
+            // exp2(-inf) = 0; hardware round-to-nearest-even to bf16
+            const uint32_t pa = __builtin_bit_cast(uint16_t, (__bf16)exp2f(z[gi][2 * pr] - mb));
+            const uint32_t pc = __builtin_bit_cast(uint16_t, (__bf16)exp2f(z[gi][2 * pr + 1] - mb));
             psum += bf_lo(pa) + bf_lo(pc);
             pw[gi][pr] = pa | (pc << 16);
           }
