@@ -1711,19 +1711,34 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_mfma_kernel(
 #pragma unroll
   for (int n = 0; n < 8; ++n) O[n] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Selection entries of a round's list positions, requested one round ahead
+  // so that their latency hides behind the previous round's tiles.
+  int32_t se[RND / 64];
+  auto fetch_sel = [&](int r0) {
+#pragma unroll
+    for (int e = 0; e < RND / 64; ++e) {
+      const int i = r0 + 64 * e + lane;
+      se[e] = (g.r > 0 && i < L.nsel_tok) ? srow[i >> g.log2r] : -1;
+    }
+  };
+  fetch_sel(0);
   for (int r0 = 0; r0 < L.n_list; r0 += RND) {
-    // Resolve this round's cache rows (4 independent chains per lane).
+    // Resolve this round's cache rows (list order: selected blocks, then the tail).
 #pragma unroll
     for (int e = 0; e < RND / 64; ++e) {
       const int i = r0 + 64 * e + lane;
       int32_t rv = -1;
       if (i < L.n_list) {
-        const int s = list_token(g, L, srow, i);
+        int s;
+        if (g.r == 0) s = i;
+        else if (i < L.nsel_tok) s = (se[e] >= 0 && se[e] < L.nb) ? (se[e] << g.log2r) + (i & (g.r - 1)) : -1;
+        else s = L.tail0 + (i - L.nsel_tok);
         const int64_t rr = (s >= 0 && s <= qp.p) ? kv_row(g, qp.b, kvh, s) : -1;
         rv = rr >= 0 ? (int32_t)(rr / D) : -1;
       }
       rows[64 * e + lane] = rv;
     }
+    fetch_sel(r0 + RND);
     wave_sync();
     const int r1 = min(r0 + RND, L.n_list);
     for (int it = r0; it < r1; it += 64) {
