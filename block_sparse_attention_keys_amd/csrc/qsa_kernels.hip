@@ -9,9 +9,14 @@
 //                 selection reproducible bit for bit).
 //   select        per-query top-k by (score desc, index asc): 4-pass 8-bit radix
 //                 select in LDS, then an ascending compaction.
-//   attn_split    gated GQA softmax attention over the selected blocks + tail,
-//                 split along the selection list; one wave per (token, KV head,
-//                 split); online softmax in base 2.
+//   attn_decode   gated GQA softmax attention over the selected blocks + tail
+//                 for decode-shaped calls (bf16, D = 128): 4-wave workgroups on
+//                 splits of the selection list, QK and PV on bf16 MFMA, the
+//                 top-k made in the kernel when it is given the scores.
+//   attn_prefill_mfma  the same for prefill-sized calls: one wave per (token,
+//                 KV head), QK and PV on bf16 MFMA.
+//   attn_split    the generic form (fp32, D = 64): one wave per (token, KV
+//                 head, split); online softmax in base 2.
 //   attn_combine  log-sum-exp merge of the splits and the sigmoid output gate.
 //
 // Semantics follow the QSA description of the Qwen4-Exp pages: MTPLX "Native
@@ -1123,11 +1128,12 @@ __global__ __launch_bounds__(64) void attn_split_kernel(
 //     16 v_mfma_f32_16x16x32_bf16;
 //   online softmax in base 2 on the accumulator layout (a lane holds one head
 //     for 16 tokens: in-lane max, then two cross-row exchanges); p rounded to
-//     bf16 (the denominator sums the same rounded values) and staged in LDS as
-//     token pairs;
-//   PV on the vector ALU: a lane holds 4 dims of 32 tokens of V (8-byte
-//     chunks, two full rows per load instruction) and accumulates bf16 dot2
-//     over token pairs, the p pairs read from LDS as broadcasts.
+//     bf16 (the denominator sums the same rounded values) and kept in
+//     registers;
+//   PV on the matrix cores: p is the A operand as it sits in the accumulator
+//     layout; V (a lane loads 4 dims of 32 tokens: 8-byte chunks, two full
+//     rows per load instruction) goes to LDS in two 32-token phases and comes
+//     back as the B operand through transposing reads: 16 MFMAs per tile.
 // The next tile's K is requested after this tile's softmax and its V after
 // this tile's PV, so each wave keeps a tile of loads in flight while it
 // computes (requesting K right after QK, with more in flight, streams slower).  The loads are unconditional (a wave's last look-ahead reads
