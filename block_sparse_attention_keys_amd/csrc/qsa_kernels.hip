@@ -243,16 +243,18 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
   // The token that ends block j pools it.  Rows appended by this same call are
   // read from kI_new (another workgroup may not have stored them yet); older
   // rows come from the cache.  The rows are staged in LDS by all threads in
-  // parallel (64 at a time); then one thread per column adds them in token
-  // order, so the sum is the sequential fp32 sum.
+  // parallel (32 at a time: 16 KB, which leaves room for 8 workgroups per CU);
+  // then one thread per column adds them in token order, so the sum is the
+  // sequential fp32 sum.
   if (pooled == nullptr || g.r == 0 || ((qp.p + 1) & (g.r - 1)) != 0) return;
-  __shared__ float stage[64 * 128];
+  constexpr int kStageRows = 32;
+  __shared__ float stage[kStageRows * 128];
   const int j = qp.p >> g.log2r;
   const int past = g.past_len[qp.b], t0 = g.cu_q[qp.b];
   const int dI = g.dI;
   float acc = 0.0f;
-  for (int s0 = j << g.log2r; s0 <= qp.p; s0 += 64) {
-    const int nrow = min(64, qp.p + 1 - s0);
+  for (int s0 = j << g.log2r; s0 <= qp.p; s0 += kStageRows) {
+    const int nrow = min(kStageRows, qp.p + 1 - s0);
     for (int e = tid; e < nrow * dI; e += blockDim.x) {
       const int rr = e / dI, x = e - rr * dI;
       const int s = s0 + rr;
