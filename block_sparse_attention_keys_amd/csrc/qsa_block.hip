@@ -254,108 +254,83 @@ __device__ QueryPosB token_pos(const Geo& g, int t) {
   return {p, p >= 0 && p < g.cap};
 }
 
-// Rotate-half RoPE of value x of a row in LDS with this token's factors
-// c[i] = cos(pos * freq_i), sn[i] = sin(pos * freq_i) (fp64 angle, rounded to
-// fp32); the rotation is fp32 (products rounded, then the sum).
-__device__ __forceinline__ float rope_cs(const float* row, int x, int R, const float* c,
-                                         const float* sn) {
-  if (x >= R) return row[x];
-  const int h = R >> 1, i = x < h ? x : x - h;
-  if (x < h) return row[x] * c[i] - row[x + h] * sn[i];
-  return row[x] * c[i] + row[i] * sn[i];
-}
-
-// One workgroup per token; each wave takes rows wid, wid + 4, ... of the
-// stacked input projection (q heads, gate heads, k heads, v heads,
-// indexer-query heads, the indexer key), kPrepBatch rows' partial sums
-// requested at once.  Lane l holds values l and l + 64 of a row.  The
-// token's rotary factors are computed once (one thread per frequency, fp64
-// cos/sin, the large-argument path included) and shared by every head.
-constexpr int kPrepBatch = 4;
-
+// Grid (token, group of 4 rows); one wave per row of the stacked input
+// projection: q heads, gate heads, k heads, v heads, indexer-query heads,
+// the indexer key.  Lane l holds values l and l + 64 of a row.
 __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a) {
   __shared__ float rowbuf[4][128];
-  __shared__ float cs[2][2][64];  // [main, indexer][cos, sin][frequency]
   const int t = blockIdx.x, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (g.r > 0 && threadIdx.x < g.HI) a.w[(int64_t)t * g.HI + threadIdx.x] = 1.0f;
+  if (g.r > 0 && blockIdx.y == 0 && threadIdx.x < g.HI) a.w[(int64_t)t * g.HI + threadIdx.x] = 1.0f;
   const QueryPosB qp = token_pos(g, t);
   const int64_t pos = qp.ok ? qp.p : 0;
-  if (threadIdx.x < 128) {
-    const int tab = threadIdx.x >> 6, i = threadIdx.x & 63;
-    const int R = tab ? g.idx_rope_dim : a.rotary_dim;
-    if (2 * i < R) {
-      // (a direct index into each table: no table chosen at run time)
-      double ang;
-      if (tab) ang = (double)pos * a.idx_freq[i];
-      else ang = (double)pos * a.freq[i];
-      cs[tab][0][i] = (float)cos(ang);
-      cs[tab][1][i] = (float)sin(ang);
-    }
-  }
-  __syncthreads();
   const int D = g.D, Hq = g.Hq, Hkv = g.Hkv, HI = g.HI, dI = g.dI;
   const int n_rows = 2 * Hq + 2 * Hkv + (g.r > 0 ? HI + 1 : 0);
   const int64_t MN = (int64_t)g.T * a.n_in;
   const float* P = a.part + (int64_t)t * a.n_in;
   float* row = rowbuf[wid];
-  for (int rb = 0; rb < n_rows; rb += 4 * kPrepBatch) {
-    int kind[kPrepBatch], head[kPrepBatch], base[kPrepBatch], len[kPrepBatch];
-    float v[kPrepBatch][2];
+  const int rw = blockIdx.y * 4 + wid;
+  if (rw < n_rows) {
+    int kind, head, base, len;  // kind: 0 q, 1 gate, 2 k, 3 v, 4 indexer q, 5 indexer k
+    if (rw < Hq) { kind = 0; head = rw; base = head * D; len = D; }
+    else if (rw < 2 * Hq) { kind = 1; head = rw - Hq; base = (Hq + head) * D; len = D; }
+    else if (rw < 2 * Hq + Hkv) { kind = 2; head = rw - 2 * Hq; base = (2 * Hq + head) * D; len = D; }
+    else if (rw < 2 * Hq + 2 * Hkv) {
+      kind = 3; head = rw - 2 * Hq - Hkv; base = (2 * Hq + Hkv + head) * D; len = D;
+    } else if (rw < 2 * Hq + 2 * Hkv + HI) {
+      kind = 4; head = rw - 2 * Hq - 2 * Hkv; base = (2 * Hq + 2 * Hkv) * D + head * dI; len = dI;
+    } else {
+      kind = 5; head = 0; base = (2 * Hq + 2 * Hkv) * D + HI * dI; len = dI;
+    }
+    float v[2];
 #pragma unroll
-    for (int j = 0; j < kPrepBatch; ++j) {
-      // kind: 0 q, 1 gate, 2 k, 3 v, 4 indexer q, 5 indexer k, -1 none
-      const int rw = rb + wid + 4 * j, kv0 = 2 * Hq + 2 * Hkv;
-      if (rw >= n_rows) { kind[j] = -1; head[j] = 0; base[j] = 0; len[j] = 0; }
-      else if (rw < Hq) { kind[j] = 0; head[j] = rw; base[j] = rw * D; len[j] = D; }
-      else if (rw < 2 * Hq) { kind[j] = 1; head[j] = rw - Hq; base[j] = rw * D; len[j] = D; }
-      else if (rw < 2 * Hq + Hkv) { kind[j] = 2; head[j] = rw - 2 * Hq; base[j] = rw * D; len[j] = D; }
-      else if (rw < kv0) { kind[j] = 3; head[j] = rw - 2 * Hq - Hkv; base[j] = rw * D; len[j] = D; }
-      else if (rw < kv0 + HI) { kind[j] = 4; head[j] = rw - kv0; base[j] = kv0 * D + (rw - kv0) * dI; len[j] = dI; }
-      else { kind[j] = 5; head[j] = 0; base[j] = kv0 * D + HI * dI; len[j] = dI; }
+    for (int e = 0; e < 2; ++e) {
+      const int x = lane + 64 * e;
+      v[e] = x < len ? sum_parts(P, a.S, MN, base + x) : 0.0f;
+    }
+    if (kind == 0 || kind == 2) {
+      // RMSNorm over the head, weight (1 + w).
+      const float ss = wave_sum(v[0] * v[0] + v[1] * v[1]);
+      const float inv = 1.0f / sqrtf(ss / (float)len + a.eps);
+      const uint16_t* w = kind == 0 ? a.q_norm : a.k_norm;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int x = lane + 64 * e;
-        v[j][e] = x < len[j] ? sum_parts(P, a.S, MN, base[j] + x) : 0.0f;
+        if (x < len) v[e] = (v[e] * inv) * (1.0f + to_f32(w[x]));
       }
     }
+    if (kind == 0 || kind == 2 || kind == 4) {
+      const int R = kind == 4 ? g.idx_rope_dim : a.rotary_dim;
+      if (R > 0) {
 #pragma unroll
-    for (int j = 0; j < kPrepBatch; ++j) {
-      const int kd = kind[j], L = len[j], hd = head[j];
-      if (kd < 0) continue;  // uniform over the wave
-      float w0 = v[j][0], w1 = v[j][1];
-      if (kd == 0 || kd == 2) {
-        // RMSNorm over the head, weight (1 + w).
-        const float ss = wave_sum(w0 * w0 + w1 * w1);
-        const float inv = 1.0f / sqrtf(ss / (float)L + a.eps);
-        const uint16_t* wn = kd == 0 ? a.q_norm : a.k_norm;
-        if (lane < L) w0 = (w0 * inv) * (1.0f + to_f32(wn[lane]));
-        if (lane + 64 < L) w1 = (w1 * inv) * (1.0f + to_f32(wn[lane + 64]));
-      }
-      if (kd == 0 || kd == 2 || kd == 4) {
-        const int tab = kd == 4 ? 1 : 0;
-        const int R = tab ? g.idx_rope_dim : a.rotary_dim;
-        if (R > 0) {
-          if (lane < L) row[lane] = w0;
-          if (lane + 64 < L) row[lane + 64] = w1;
-          wave_sync();
-          const float r0 = lane < L ? rope_cs(row, lane, R, cs[tab][0], cs[tab][1]) : 0.0f;
-          const float r1 = lane + 64 < L ? rope_cs(row, lane + 64, R, cs[tab][0], cs[tab][1]) : 0.0f;
-          wave_sync();  // the row buffer is rewritten by the next row
-          w0 = r0;
-          w1 = r1;
+        for (int e = 0; e < 2; ++e)
+          if (lane + 64 * e < len) row[lane + 64 * e] = v[e];
+        wave_sync();
+        float rv[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int x = lane + 64 * e;
+          // (one call per table: no pointer chosen at run time)
+          rv[e] = x >= len ? 0.0f
+                  : kind == 4 ? rope_at(row, x, R, a.idx_freq, pos)
+                              : rope_at(row, x, R, a.freq, pos);
         }
+        v[0] = rv[0];
+        v[1] = rv[1];
       }
-      uint16_t* dst;
-      switch (kd) {
-        case 0: dst = a.q + ((int64_t)t * Hq + hd) * D; break;
-        case 1: dst = a.gate + ((int64_t)t * Hq + hd) * D; break;
-        case 2: dst = a.k + ((int64_t)t * Hkv + hd) * D; break;
-        case 3: dst = a.v + ((int64_t)t * Hkv + hd) * D; break;
-        case 4: dst = a.q_idx + ((int64_t)t * HI + hd) * dI; break;
-        default: dst = a.k_idx + (int64_t)t * dI; break;
-      }
-      if (lane < L) dst[lane] = bf16_rne(w0);
-      if (lane + 64 < L) dst[lane + 64] = bf16_rne(w1);
+    }
+    uint16_t* dst;
+    switch (kind) {
+      case 0: dst = a.q + ((int64_t)t * Hq + head) * D; break;
+      case 1: dst = a.gate + ((int64_t)t * Hq + head) * D; break;
+      case 2: dst = a.k + ((int64_t)t * Hkv + head) * D; break;
+      case 3: dst = a.v + ((int64_t)t * Hkv + head) * D; break;
+      case 4: dst = a.q_idx + ((int64_t)t * HI + head) * dI; break;
+      default: dst = a.k_idx + (int64_t)t * dI; break;
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int x = lane + 64 * e;
+      if (x < len) dst[x] = bf16_rne(v[e]);
     }
   }
 }
@@ -403,8 +378,7 @@ hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, h
 
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st) {
   const int n_rows = 2 * g.Hq + 2 * g.Hkv + (g.r > 0 ? g.HI + 1 : 0);
-  (void)n_rows;
-  block_prep_kernel<<<g.T, 256, 0, st>>>(g, a);
+  block_prep_kernel<<<dim3(g.T, (n_rows + 3) / 4), 256, 0, st>>>(g, a);
   return hipGetLastError();
 }
 
