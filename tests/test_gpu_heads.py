@@ -54,3 +54,24 @@ def test_mfma_prefill_head_groupings(hq, hkv):
     seqf = SeqF32(case)
     for i in sorted(res):
         check_call(dc, seqf, res[i], sample=48, rng_seed=i)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 16), (16, 8), (16, 4), (16, 1), (12, 3)])
+def test_decode_8bit_cache_head_groupings(hq, hkv):
+    """The 8-bit (E4M3) cache across head groupings: in the Hadamard basis
+    where the library supports it (4 or more query heads per KV head: the
+    query is rotated across lanes), plain codes otherwise, where a rotated
+    cache is refused with QSA_ERR_UNSUPPORTED."""
+    case = _case("ragged_paged_decode_128k_bf16", hq, hkv, n_seqs=3, ctx_lo=1500, ctx_hi=6000,
+                 steps=2)
+    rotate = hq // hkv >= 4
+    say(f"8-bit decode Hq={hq} Hkv={hkv} rotate={rotate} ctx={case.ctx}")
+    if not rotate:
+        with pytest.raises(qsa.QsaError) as err:
+            runner.DeviceCase(case, kv_fp8=True, kv_rotate=True)
+        assert err.value.status == qsa.QSA_ERR_UNSUPPORTED
+    dc = runner.DeviceCase(case, kv_fp8=True, kv_rotate=rotate)
+    res = run_calls(dc)
+    seqf = SeqF32(case)
+    for i in sorted(res):
+        check_call(dc, seqf, res[i])
