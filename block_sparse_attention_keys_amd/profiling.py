@@ -168,17 +168,23 @@ def read_summary(path: str) -> Dict[str, str]:
 
 
 def cmd_pmc(a) -> None:
-    """Mean per dispatch of every counter in a --pmc run, for the kernels
+    """Mean per dispatch of every counter in one or more --pmc runs (one
+    --dir and one --cmd per run, in the same order), for the kernels
     matching --kernel."""
-    path = _one(os.path.join(a.dir, "**", "*counter_collection.csv"))
+    if len(a.dir) != len(a.cmd):
+        raise SystemExit("give one --cmd per --dir")
+    shas = {measured_sha256(d) for d in a.dir}
+    if len(shas) != 1:
+        raise SystemExit(f"the runs were measured on different sources: {sorted(shas)}")
     per: Dict[tuple, List[float]] = {}
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            if re.search(a.kernel, r["Kernel_Name"]):
-                per.setdefault((_short(r["Kernel_Name"]), r["Counter_Name"]), []).append(
-                    float(r["Counter_Value"]))
-    lines = [f"# {a.title}", "", f"command: {a.cmd}",
-             f"kernel_source_sha256: {measured_sha256(a.dir)}", "",
+    for d in a.dir:
+        with open(_one(os.path.join(d, "**", "*counter_collection.csv"))) as f:
+            for r in csv.DictReader(f):
+                if re.search(a.kernel, r["Kernel_Name"]):
+                    per.setdefault((_short(r["Kernel_Name"]), r["Counter_Name"]), []).append(
+                        float(r["Counter_Value"]))
+    lines = [f"# {a.title}", ""] + [f"command: {c}" for c in a.cmd] + [
+             f"kernel_source_sha256: {shas.pop()}", "",
              "| kernel | counter | dispatches | mean per dispatch |", "|---|---|---|---|"]
     for (k, c), v in sorted(per.items()):
         lines.append(f"| {k} | {c} | {len(v)} | {statistics.mean(v):.6g} |")
@@ -202,7 +208,9 @@ def main() -> None:
     t.add_argument("--note", default="")
     sub.add_parser("sha")
     q = sub.add_parser("pmc")
-    for k in ("dir", "cmd", "title", "out", "kernel"):
+    for k in ("dir", "cmd"):
+        q.add_argument("--" + k, required=True, action="append")
+    for k in ("title", "out", "kernel"):
         q.add_argument("--" + k, required=True)
     q.add_argument("--note", default="")
     c = sub.add_parser("counters")
