@@ -171,3 +171,15 @@ def test_pages_worked_count_measured(probe):
         say(f"  ratio {r}: rows loaded {got} = {hkv} x {got // hkv}; the pages' count {total} = 8 x "
             f"{total // 8}")
         assert got == want
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 1), (16, 4), (12, 3)])
+def test_mfma_prefill_placement_loads_each_unit_once(probe, hq, hkv):
+    """The prefill kernel places workgroups by KV head when Hkv divides the 8
+    XCDs (a plain order otherwise): every (token, KV head) unit must run
+    exactly once, which the row count shows (a unit run twice writes the same
+    output, so parity alone would not)."""
+    import dataclasses
+    sp = dataclasses.replace(workloads.SPECS["chunked_prefill_32k_bf16"], n_q_heads=hq,
+                             n_kv_heads=hkv, prefill_len=2 * 600 + 37, chunk=600)
+    _count_core(probe, workloads._draw(sp, 0), calls={0, 1, 2})
