@@ -125,8 +125,9 @@ def block(orc, bd: dict, x, W_in, qn_w, kn_w, W_o, q_pos, want_scores: bool = Fa
           nb_cap: Optional[int] = None, kv8: Optional[tuple] = None) -> dict:
     """The QSA block for the queries at positions q_pos of ONE sequence whose
     tokens 0..n-1 have hidden states x [n][d_model] (the caches hold all of
-    them).  Returns y [nq][d_model] (fp32), the selections, and the
-    intermediate bf16-valued tensors of the queries.  kv8 = (rotate,
+    them).  Returns y [nq][d_model] (fp32), the selections, the
+    intermediate bf16-valued tensors of the queries ("front") and the k, v
+    and indexer-key rows of every token ("front_kv").  kv8 = (rotate,
     k_scale, v_scale): the K/V cache holds 8-bit codes of the block's k and
     v (the oracle's own encoding, qsa_oracle_kv8_encode)."""
     x = widen(x)
@@ -151,4 +152,5 @@ def block(orc, bd: dict, x, W_in, qn_w, kn_w, W_o, q_pos, want_scores: bool = Fa
     ref["attn"] = attn
     ref["y"] = project(attn, W_o)
     ref["front"] = qs
+    ref["front_kv"] = kv
     return ref

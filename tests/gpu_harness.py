@@ -77,15 +77,39 @@ def run_calls(dc: runner.DeviceCase, calls: Optional[List[int]] = None, keep=Non
     return res
 
 
+def kv8_values(orc, codes, rotate: bool, scale: float) -> np.ndarray:
+    """fp32 K or V rows that 8-bit codes [..., D] stand for, back in the
+    unrotated basis (decode(c) * scale, then H x / D when rotated): the
+    input of an oracle attention over a token set the GPU chose."""
+    lut = orc.e4m3_decode(np.arange(256, dtype=np.uint8))
+    x = lut[np.asarray(codes)] * np.float32(scale)
+    if rotate:
+        x = orc.fwht(x) / np.float32(x.shape[-1])
+    return x.astype(np.float32)
+
+
+def attend_over_selection(orc, dims, K, V, q, gate, sel_row, n_blocks: int, p: int):
+    """The oracle's gated attention of one query at position p over the token
+    set of a given selection (blocks sel_row[:n_blocks] plus the tail)."""
+    r = dims["block_size"]
+    toks = orc.token_set(np.asarray(sel_row[:n_blocks], np.int32), r, p)
+    scale = dims["attn_scale"] if dims["attn_scale"] > 0 else dims["head_dim"] ** -0.5
+    return orc.attend(q, K, V, gate, toks, scale)
+
+
 def check_call(dc, seqf: SeqF32, result, sample: Optional[int] = None, rng_seed: int = 0,
-               orc=None) -> dict:
+               orc=None, max_exempt: int = 0) -> dict:
     """Compare one call's GPU results with the oracle, all queries or a sample
-    of them per sequence.  Raises AssertionError on a miss."""
+    of them per sequence.  Selections first (bit-exact, or a valid near-tie
+    row, at most max_exempt of them: 0 wherever the scores are bit-exact);
+    then outputs, a near-tie row's against the oracle's attention over the
+    GPU's own selection.  Raises AssertionError on a miss."""
     orc = orc or oracle.load()
     out, sel, nblk, spans = result
     case = dc.case
     dims = dims_of(dc)
     dtype = case.spec.dtype
+    kv8 = getattr(dc, "kv8", False)
     rng = np.random.default_rng(rng_seed)
     t0 = 0
     worst = {"max_abs": 0.0, "mean_abs": 0.0, "max_rel": 0.0, "rows": 0, "exempt": 0}
@@ -97,7 +121,7 @@ def check_call(dc, seqf: SeqF32, result, sample: Optional[int] = None, rng_seed:
         K, V, kI = seqf.get(b)
         qbase = int(case.q_pos[b][0])
         qi = (s - qbase) + idx
-        if getattr(dc, "kv8", False):
+        if kv8:
             Kc, Vc = seqf.codes(b, dc, orc)
             ref = orc.sequence_kv8(dims, Kc, Vc, dc.kv_rotate, dc.k_scale, dc.v_scale, kI,
                                    s + idx, case.q[b][qi], case.qI[b][qi], case.w[b][qi],
@@ -106,18 +130,32 @@ def check_call(dc, seqf: SeqF32, result, sample: Optional[int] = None, rng_seed:
             ref = orc.sequence(dims, K, V, kI, s + idx, case.q[b][qi], case.qI[b][qi],
                                case.w[b][qi], case.gate[b][qi],
                                want_scores=dims["block_size"] > 0)
-        got = out[t0 + idx]
-        ok, st = parity.outputs_ok(got, ref["out"], dtype)
-        assert ok, f"seq {b} outputs {st}"
+        ref_out = ref["out"]
         if dims["block_size"] > 0:
             r = dims["block_size"]
             nb = (s + idx + 1) // r
             k = ref["sel"].shape[1]
-            oks, ndiff, nex = parity.selections_ok(sel[t0 + idx][:, :k], nblk[t0 + idx],
-                                                   ref["sel"], ref["n_blocks"],
-                                                   ref.get("scores"), nb)
+            got_sel = sel[t0 + idx][:, :k]
+            oks, ndiff, ex = parity.selections_ok(got_sel, nblk[t0 + idx], ref["sel"],
+                                                  ref["n_blocks"], ref.get("scores"), nb)
             assert oks, f"seq {b}: selections differ in {ndiff} rows"
-            worst["exempt"] += nex
+            worst["exempt"] += len(ex)
+            assert worst["exempt"] <= max_exempt, (
+                f"seq {b}: {worst['exempt']} near-tie rows (allowed {max_exempt})")
+            if ex:
+                ref_out = ref_out.copy()
+                if kv8:
+                    Kx = kv8_values(orc, Kc, dc.kv_rotate, dc.k_scale)
+                    Vx = kv8_values(orc, Vc, dc.kv_rotate, dc.v_scale)
+                else:
+                    Kx, Vx = K, V
+                for i in ex:
+                    ref_out[i] = attend_over_selection(orc, dims, Kx, Vx, case.q[b][qi[i]],
+                                                       case.gate[b][qi[i]], got_sel[i],
+                                                       int(ref["n_blocks"][i]), int(s + idx[i]))
+        got = out[t0 + idx]
+        ok, st = parity.outputs_ok(got, ref_out, dtype)
+        assert ok, f"seq {b} outputs {st}"
         for kk in ("max_abs", "mean_abs", "max_rel"):
             worst[kk] = max(worst[kk], st[kk])
         worst["rows"] += len(idx)

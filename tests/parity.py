@@ -1,23 +1,40 @@
 """Parity comparators between the HIP path and the CPU oracle.
 
 Bars (written here, used by every GPU parity test):
-  selections  bit-exact; a row may differ only where the oracle's k-th and
+  selections  bit-exact.  A row may differ only where the oracle's k-th and
               (k+1)-th block scores are a near tie: |s_k - s_k+1| <=
               1e-5 * max(|s_k|, |s_k+1|), or both are below 1e-5 * the row's
               largest score (a relu boundary, a tiny positive next to +0).
+              Such a row must still be a valid selection: the same count,
+              distinct ids in [0, nb), ascending, -1 padded, and equal to the
+              oracle's set except for blocks whose oracle scores lie inside
+              that tie band around the k-th score.  Its output is then
+              compared with the oracle's attention over the GPU's own token
+              set.  Where scores are bit-exact (every path whose indexer
+              inputs are the seeded draws) the tests require zero such rows.
   outputs     bf16: max-abs <= 2e-2 and mean-abs <= 2e-3, and per (token,
               head) ||out - ref||_2 <= 2e-2 ||ref||_2 (at the workloads' data
               scale the outputs are ~1e-3, so the absolute bounds alone
               would pass an all-zero output); fp32: max-abs <= 1e-4 and the
               same relative bound at 1e-4.
-  block       (qsa_block_forward: the indexer's inputs come out of bf16
-              projections whose fp32 sums run in a different order on each
-              side, so an indexer value can differ by one bf16 step, about
-              2^-8 of it.)  A row's selection may then differ from the
-              oracle's, but every block the GPU keeps must score within
-              BLOCK_SCORE_REL of the row's largest score below the oracle's
-              k-th score, with the same count; at most 10 % of the rows may
-              differ, and outputs are compared on the rows that agree.
+  block       (qsa_block_forward.)  The k, v and indexer-key rows the block
+              writes into the caches must lie within one bf16 ulp of the
+              oracle's front end, element by element, plus ROW_SLACK times
+              the row's largest magnitude: the projections' fp32 sums run in
+              a different order on each side, so a rounding to bf16 can land
+              one step apart, and where RoPE or a dot product cancels to a
+              value much smaller than its row, that fp32 difference can reach
+              beyond one step of the small value.  The pooled keys must equal
+              the oracle's pooling and rotation of the GPU's own indexer-key
+              rows bit for bit.  The only unverified input of the scores is
+              then the indexer query, within the same bar per element: a
+              block's score can move by at most B_j = c sum_h w_h sum_x
+              dq_hx |kbar_jx| (relu is 1-Lipschitz; dq_hx the bar at q_hx),
+              slightly widened for fp32 rounding.  A row's selection is valid
+              when some scores inside those bands rank it first: min over
+              kept (s_j + B_j) >= max over dropped (s_i - B_i).  Every row's
+              output is compared with the oracle's block over the GPU's own
+              selection.
 """
 from __future__ import annotations
 
@@ -26,8 +43,12 @@ import numpy as np
 BF16_MAX_ABS, BF16_MEAN_ABS, BF16_REL = 2e-2, 2e-3, 2e-2
 F32_MAX_ABS, F32_REL = 1e-4, 1e-4
 TIE_REL = 1e-5
-BLOCK_SCORE_REL = 1e-2
-BLOCK_ROWS_DIFFERING = 0.10
+# fp32 rounding slack on a block's score band (both sides sum in the same
+# order; only their inputs differ): 2^-16 of the band's own scale.
+BLOCK_BAND_SLACK = 2.0 ** -16
+# fp32 sum-order slack of a block front-end value, relative to its row's
+# largest magnitude (16 times finer than one bf16 step at that magnitude).
+ROW_SLACK = 2.0 ** -12
 
 
 def output_stats(got, ref) -> dict:
@@ -66,38 +87,105 @@ def near_tie(scores_row: np.ndarray, nb: int, k: int) -> bool:
     return abs(a) <= TIE_REL * top and abs(b) <= TIE_REL * top
 
 
+def tie_band(scores_row: np.ndarray, nb: int, k: int) -> np.ndarray:
+    """Blocks 0..nb-1 whose oracle score is a near tie with the k-th largest
+    (the same rule as near_tie, applied to every block)."""
+    s = np.asarray(scores_row[:nb], np.float64)
+    if nb <= k or nb == 0:
+        return np.zeros(nb, bool)
+    kth = np.sort(s)[::-1][k - 1]
+    top = max(float(np.abs(s).max()), 1e-30)
+    rel = np.abs(s - kth) <= TIE_REL * np.maximum(np.abs(s), abs(kth))
+    low = (np.abs(s) <= TIE_REL * top) & (abs(kth) <= TIE_REL * top)
+    return rel | low
+
+
+def row_well_formed(row: np.ndarray, n: int, nb: int) -> bool:
+    """n distinct ascending ids in [0, nb), then -1 padding."""
+    row = np.asarray(row)
+    got = row[:n]
+    return (bool((row[n:] == -1).all()) and bool((got >= 0).all()) and bool((got < nb).all())
+            and bool((np.diff(got) > 0).all()))
+
+
+def tie_row_valid(got_row, ref_row, n: int, scores_row, nb: int, k: int) -> bool:
+    """A differing row: well formed, and the same set as the oracle's except
+    for blocks inside the tie band around the oracle's k-th score."""
+    if not near_tie(scores_row, nb, k) or not row_well_formed(got_row, n, nb):
+        return False
+    band = tie_band(scores_row, nb, k)
+    got = set(np.asarray(got_row[:n]).tolist())
+    ref = set(np.asarray(ref_row[:n]).tolist())
+    return all(band[j] for j in got ^ ref)
+
+
 def selections_ok(sel_gpu, nblk_gpu, sel_ref, nblk_ref, scores_ref=None, nb=None):
-    """Returns (ok, n_rows_differing, n_rows_exempted)."""
+    """Returns (ok, n_rows_differing, exempted row indices).  A differing row
+    passes only as a valid near-tie row (tie_row_valid)."""
     sel_gpu = np.asarray(sel_gpu)
     sel_ref = np.asarray(sel_ref)
     if not np.array_equal(np.asarray(nblk_gpu), np.asarray(nblk_ref)):
-        return False, -1, 0
+        return False, -1, []
     diff = np.where((sel_gpu != sel_ref).any(axis=1))[0]
-    exempt = 0
+    exempt = []
+    k = sel_ref.shape[1]
     for i in diff:
-        if scores_ref is None or nb is None or not near_tie(scores_ref[i], int(nb[i]),
-                                                            sel_ref.shape[1]):
+        if scores_ref is None or nb is None:
             return False, len(diff), exempt
-        exempt += 1
+        if not tie_row_valid(sel_gpu[i], sel_ref[i], int(nblk_ref[i]), scores_ref[i], int(nb[i]),
+                             k):
+            return False, len(diff), exempt
+        exempt.append(int(i))
     return True, len(diff), exempt
 
 
-def block_selection_rows(sel_gpu, nblk_gpu, sel_ref, nblk_ref, scores_ref, nb):
-    """Per row: 0 = identical, 1 = differs but valid under BLOCK_SCORE_REL,
-    -1 = invalid."""
-    out = np.zeros(len(sel_ref), np.int32)
-    for i in range(len(sel_ref)):
-        if int(nblk_gpu[i]) != int(nblk_ref[i]):
-            out[i] = -1
-            continue
-        n = int(nblk_ref[i])
-        if np.array_equal(sel_gpu[i][:n], sel_ref[i][:n]):
-            continue
-        s = np.asarray(scores_ref[i][:int(nb[i])], np.float64)
-        kth = np.sort(s)[::-1][n - 1]
-        tol = BLOCK_SCORE_REL * max(abs(s).max(), 1e-30)
-        got = np.asarray(sel_gpu[i][:n])
-        ok = (len(np.unique(got)) == n and (got >= 0).all() and (got < len(s)).all()
-              and (s[got] >= kth - tol).all())
-        out[i] = 1 if ok else -1
-    return out
+def bf16_ulp(x) -> np.ndarray:
+    """The spacing of bf16 values at |x| (the larger one at a power of two;
+    the smallest normal spacing at 0)."""
+    a = np.abs(np.asarray(x, np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def front_bar(ref) -> np.ndarray:
+    """Allowed |got - ref| per element of block front-end rows [..., n]: one
+    bf16 ulp at ref plus ROW_SLACK times the row's largest |ref|."""
+    ref = np.asarray(ref, np.float64)
+    rowmax = np.abs(ref).max(axis=-1, keepdims=True)
+    return bf16_ulp(ref) + ROW_SLACK * rowmax
+
+
+def within_one_ulp(got, ref) -> np.ndarray:
+    """Elementwise |got - ref| <= the front-end bar (one bf16 ulp of either
+    value, plus the row slack)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bar = np.maximum(bf16_ulp(got), bf16_ulp(ref)) + (front_bar(ref) - bf16_ulp(ref))
+    return np.abs(got - ref) <= bar
+
+
+def score_bands(qI_row, w_row, pooled, c: float) -> np.ndarray:
+    """B_j for every block of `pooled` [nb][d_I] (the GPU's stored pooled keys):
+    the most block j's score can move when each indexer-query element moves by
+    its front-end bar.  qI_row [H_I][d_I], w_row [H_I]."""
+    q = np.asarray(qI_row, np.float64)
+    w = np.abs(np.asarray(w_row, np.float64))
+    P = np.abs(np.asarray(pooled, np.float64))
+    dq = 2.0 * bf16_ulp(q) + ROW_SLACK * np.abs(q).max(axis=-1, keepdims=True)
+    per_head = dq @ P.T  # [H_I][nb]
+    band = c * (w[:, None] * per_head).sum(axis=0)
+    scale = c * (w[:, None] * (np.abs(q) @ P.T)).sum(axis=0)
+    return band * (1.0 + 2.0 ** -6) + BLOCK_BAND_SLACK * scale
+
+
+def banded_row_valid(got_row, n: int, scores_row, bands, nb: int) -> bool:
+    """Some scores within [s - B, s + B] make got_row[:n] a top-n set."""
+    if not row_well_formed(got_row, n, nb):
+        return False
+    s = np.asarray(scores_row[:nb], np.float64)
+    b = np.asarray(bands[:nb], np.float64)
+    kept = np.zeros(nb, bool)
+    kept[np.asarray(got_row[:n])] = True
+    if kept.all() or not kept.any():
+        return True
+    return float((s[kept] + b[kept]).min()) >= float((s[~kept] - b[~kept]).max())
