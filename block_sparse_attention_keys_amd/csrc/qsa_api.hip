@@ -8,10 +8,18 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "qsa.h"
 #include "qsa_internal.h"
+
+// Device scratch of qsa_forward_noalloc: its workspace (scores, selections,
+// split partials) for callers that cannot allocate.  Every GPU the library
+// runs on holds one copy until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the symbol):
+// it uses the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[QSA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -248,6 +256,57 @@ qsa_status hip_status(hipError_t e, const char* what) {
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// Pointer checks of qsa_forward / qsa_forward_noalloc (everything but the workspace).
+qsa_status check_forward_args(const Plan& pl, const void* q, const void* k_new,
+                              const void* v_new, const void* q_idx, const void* k_idx_new,
+                              const float* w, const void* gate, const void* k_cache,
+                              const void* v_cache, const void* k_idx_cache, const float* pooled,
+                              const void* out, const int32_t* sel_opt,
+                              const int32_t* n_blocks_opt) {
+  QSA_TRY(need(q, "q", 16));
+  QSA_TRY(need(k_new, "k_new", 16));
+  QSA_TRY(need(v_new, "v_new", 16));
+  QSA_TRY(need(gate, "gate", 16));
+  QSA_TRY(need(k_cache, "k_cache", 16));
+  QSA_TRY(need(v_cache, "v_cache", 16));
+  QSA_TRY(need(out, "out", 16));
+  if (pl.geo.r != 0) {
+    QSA_TRY(need(q_idx, "q_idx", 16));
+    QSA_TRY(need(k_idx_new, "k_idx_new", 16));
+    QSA_TRY(need(w, "w", 4));
+    QSA_TRY(need(k_idx_cache, "k_idx_cache", 16));
+    QSA_TRY(need(pooled, "pooled", 16));
+    if (sel_opt) QSA_TRY(need(sel_opt, "sel", 4));
+    if (n_blocks_opt) QSA_TRY(need(n_blocks_opt, "n_blocks", 4));
+  }
+  return QSA_OK;
+}
+
+// The scratch array's address on the current device, looked up once per
+// device (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+qsa_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(QSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(QSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QSA_OK;
+}
+
 qsa_status forward_launch(const Plan& pl, const qsa_batch* batch, const void* q,
                           const void* k_new, const void* v_new, const void* q_idx,
                           const void* k_idx_new, const float* w, const void* gate,
@@ -365,24 +424,33 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
   Plan pl;
   QSA_TRY(resolve(params, batch, &pl));
   if (batch->n_tokens == 0) return QSA_OK;
-  QSA_TRY(need(q, "q", 16));
-  QSA_TRY(need(k_new, "k_new", 16));
-  QSA_TRY(need(v_new, "v_new", 16));
-  QSA_TRY(need(gate, "gate", 16));
-  QSA_TRY(need(k_cache, "k_cache", 16));
-  QSA_TRY(need(v_cache, "v_cache", 16));
-  QSA_TRY(need(out, "out", 16));
-  const bool qsa_layer = pl.geo.r != 0;
-  if (qsa_layer) {
-    QSA_TRY(need(q_idx, "q_idx", 16));
-    QSA_TRY(need(k_idx_new, "k_idx_new", 16));
-    QSA_TRY(need(w, "w", 4));
-    QSA_TRY(need(k_idx_cache, "k_idx_cache", 16));
-    QSA_TRY(need(pooled, "pooled", 16));
-    if (sel_opt) QSA_TRY(need(sel_opt, "sel", 4));
-    if (n_blocks_opt) QSA_TRY(need(n_blocks_opt, "n_blocks", 4));
-  }
+  QSA_TRY(check_forward_args(pl, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cache, v_cache,
+                             k_idx_cache, pooled, out, sel_opt, n_blocks_opt));
   QSA_TRY(check_ws(pl, ws, ws_bytes));
+  return forward_launch(pl, batch, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cache, v_cache,
+                        k_idx_cache, pooled, out, sel_opt, n_blocks_opt, ws,
+                        static_cast<hipStream_t>(stream));
+}
+
+qsa_status qsa_forward_noalloc(const qsa_params* params, const qsa_batch* batch, const void* q,
+                               const void* k_new, const void* v_new, const void* q_idx,
+                               const void* k_idx_new, const float* w, const void* gate,
+                               void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                               void* out, int32_t* sel_opt, int32_t* n_blocks_opt,
+                               void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  QSA_TRY(resolve(params, batch, &pl));
+  if (batch->n_tokens == 0) return QSA_OK;
+  QSA_TRY(check_forward_args(pl, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cache, v_cache,
+                             k_idx_cache, pooled, out, sel_opt, n_blocks_opt));
+  if (pl.total > (size_t)QSA_NOALLOC_SCRATCH_BYTES)
+    return fail(QSA_ERR_WORKSPACE,
+                "this call needs %zu bytes of workspace; qsa_forward_noalloc holds %zu "
+                "(use qsa_forward with a workspace, or split the batch)",
+                pl.total, (size_t)QSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  QSA_TRY(scratch_on_current_device(&ws));
   return forward_launch(pl, batch, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cache, v_cache,
                         k_idx_cache, pooled, out, sel_opt, n_blocks_opt, ws,
                         static_cast<hipStream_t>(stream));

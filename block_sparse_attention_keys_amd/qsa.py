@@ -28,7 +28,8 @@ QSA_KV_FP8 = 2
 
 EXPORTS = ["qsa_last_error", "qsa_pooled_ld", "qsa_workspace_size", "qsa_pool_keys",
            "qsa_store_kv", "qsa_score_select", "qsa_attend", "qsa_forward",
-           "qsa_block_workspace_size", "qsa_block_forward"]
+           "qsa_forward_noalloc", "qsa_block_workspace_size", "qsa_block_forward"]
+QSA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class qsa_params(C.Structure):
@@ -93,6 +94,8 @@ def _load(path: str) -> C.CDLL:
     L.qsa_attend.argtypes = [P, B, vp, vp, vp, vp, vp, vp, vp, vp, C.c_size_t, vp]
     L.qsa_forward.restype = C.c_int
     L.qsa_forward.argtypes = [P, B] + [vp] * 15 + [C.c_size_t, vp]
+    L.qsa_forward_noalloc.restype = C.c_int
+    L.qsa_forward_noalloc.argtypes = [P, B] + [vp] * 15
     BP = C.POINTER(qsa_block_params)
     L.qsa_block_workspace_size.restype = C.c_size_t
     L.qsa_block_workspace_size.argtypes = [P, BP, B]
@@ -218,6 +221,16 @@ def qsa_forward(params, batch, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cac
                              _ptr(k_cache), _ptr(v_cache), _ptr(k_idx_cache), _ptr(pooled),
                              _ptr(out), _ptr(sel), _ptr(n_blocks), _ptr(ws), _nbytes(ws),
                              _stream(stream)))
+
+
+def qsa_forward_noalloc(params, batch, q, k_new, v_new, q_idx, k_idx_new, w, gate, k_cache,
+                        v_cache, k_idx_cache, pooled, out, sel=None, n_blocks=None,
+                        stream=None) -> None:
+    _check(lib().qsa_forward_noalloc(C.byref(params), C.byref(_b(batch)), _ptr(q), _ptr(k_new),
+                                     _ptr(v_new), _ptr(q_idx), _ptr(k_idx_new), _ptr(w),
+                                     _ptr(gate), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(k_idx_cache), _ptr(pooled), _ptr(out), _ptr(sel),
+                                     _ptr(n_blocks), _stream(stream)))
 
 
 def make_block_params(d_model, rotary_dim, rope_theta, norm_eps=1e-6) -> qsa_block_params:

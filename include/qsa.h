@@ -200,6 +200,32 @@ qsa_status qsa_forward(const qsa_params* params, const qsa_batch* batch, const v
                        void* out, int32_t* sel_opt, int32_t* n_blocks_opt, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* qsa_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches on the same kernels, with the workspace taken from a scratch
+ * array inside the library instead of a ws argument.  Arguments, results
+ * and errors as qsa_forward.
+ *   - The scratch holds QSA_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, allocated
+ *     with the library's code on each device it runs on and held until the
+ *     process ends; a call whose qsa_workspace_size exceeds it returns
+ *     QSA_ERR_WORKSPACE and launches nothing.
+ *   - No device memory is allocated or freed, by the library or by any
+ *     routine it calls; nothing in the scratch has to start at zero (every
+ *     value a call reads there, that call wrote first).
+ *   - The scratch is looked up on the calling thread's current device, which
+ *     must be the device of `stream`.
+ *   - All calls on one GPU share its scratch: calls that overlap in time on
+ *     one GPU (different streams, or different host threads without
+ *     ordering) race and give undefined results; calls ordered on one
+ *     stream are fine. */
+#define QSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+qsa_status qsa_forward_noalloc(const qsa_params* params, const qsa_batch* batch, const void* q,
+                               const void* k_new, const void* v_new, const void* q_idx,
+                               const void* k_idx_new, const float* w, const void* gate,
+                               void* k_cache, void* v_cache, void* k_idx_cache, float* pooled,
+                               void* out, int32_t* sel_opt, int32_t* n_blocks_opt,
+                               void* stream);
+
 /* ------------------------------------------------------------------------
  * The QSA attention block around the path (llama.cpp PR #27739 page,
  * LocalAI QSA-block commit, opening paragraph: q/k/v/o projections, the

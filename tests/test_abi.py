@@ -256,3 +256,21 @@ def test_probe_symbols_only_in_the_probe_build(L):
         assert not hasattr(L, n), f"{n} leaked into the product library"
     for n in declared_functions():
         assert hasattr(P, n), n
+
+
+def test_noalloc_entry_validates_before_touching_the_gpu(L):
+    """qsa_forward_noalloc: the same argument checks as qsa_forward, and a call
+    whose workspace exceeds the library's scratch is rejected before any HIP
+    call (nothing here has a GPU)."""
+    def call(p, b, ptr=FAKE):
+        return L.qsa_forward_noalloc(C.byref(p), C.byref(b), *([ptr] * 14), None)
+
+    assert call(P(n_kv_heads=3), Bt()) == qsa.QSA_ERR_INVALID
+    assert call(P(), Bt(), ptr=FAKE + 2) == qsa.QSA_ERR_INVALID
+    assert "aligned" in qsa.last_error()
+    big = Bt(n_tokens=8192, max_q_len=8192, max_kv_len=131072, kv_capacity=131072)
+    assert qsa.qsa_workspace_size(P(), big) > qsa.QSA_NOALLOC_SCRATCH_BYTES
+    assert call(P(), big) == qsa.QSA_ERR_WORKSPACE
+    assert "qsa_forward_noalloc holds" in qsa.last_error()
+    b0 = Bt(n_tokens=0, cu_q=None, past_len=None)
+    assert call(P(), b0, ptr=None) == qsa.QSA_OK
