@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libqsa.so")
 # debug build for tests: counts the K/V rows the attention kernels load
 PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
 PROBE_FLAGS = ["-DQSA_COUNT_KEYS"]
-SOURCES = ["qsa_api.hip", "qsa_kernels.hip", "qsa_block.hip"]
+SOURCES = ["qsa_api.hip", "qsa_kernels.hip", "qsa_block.hip", "qsa_prefill_ks.hip"]
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -54,6 +54,9 @@ struct Plan {
   qsa::AttnPlan attn;
   int elem;
   size_t off_scores, off_sel, off_nblk, off_part, total;
+  // key-stationary prefill (attn.ks): entry lists, work items, partial states
+  size_t off_ks_list, off_ks_items, off_ks_hist, off_ks_boff, off_ks_po, off_ks_pl;
+  int32_t ks_sub, max_q;
 };
 
 // Validates params/batch and derives every launch size from host values only.
@@ -203,7 +206,16 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   // unit.  Few units (decode): the split-list bandwidth kernels.
   pl.attn.mfma =
       (pl.elem == qsa::kBF16 && g.D == 128 && !g.kv8 && units >= kMfmaMinUnits) ? 1 : 0;
-  if (pl.attn.mfma) pl.attn.n_splits = 1;
+  // Long prefill chunks of a QSA layer: the key-stationary path, when its
+  // entry packing and its plan's block table hold the call.
+  pl.attn.ks = (r != 0 && b.max_q_len >= qsa::kKsMinQueries && qsa::ks_supported(g, pl.elem) &&
+                g.nbcap + 1 <= qsa::kKsMaxBlocks && k + 1 <= qsa::kKsMaxSlots &&
+                (int64_t)b.n_tokens < (int64_t(1) << 20) &&
+                (int64_t)b.n_seqs * (g.nbcap + 2) <= (int64_t(1) << 16))
+                   ? 1
+                   : 0;
+  if (pl.attn.ks) pl.attn.mfma = 0;
+  if (pl.attn.mfma || pl.attn.ks) pl.attn.n_splits = 1;
   splits = pl.attn.n_splits;
 
   const int64_t T = b.n_tokens;
@@ -216,6 +228,26 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   off += round_up(T * 4, kAlign);
   pl.off_part = off;
   if (splits > 1) off += round_up(units * splits * G * (g.D + 2) * 4, kAlign);
+  pl.ks_sub = (int32_t)std::min<int64_t>(std::max<int64_t>(T, 1), qsa::kKsSubTokens);
+  pl.max_q = b.max_q_len;
+  pl.off_ks_list = pl.off_ks_items = pl.off_ks_hist = pl.off_ks_boff = pl.off_ks_po =
+      pl.off_ks_pl = off;
+  if (pl.attn.ks) {
+    const int64_t S = pl.ks_sub, k1 = k + 1;
+    pl.off_ks_list = off;
+    off += round_up(S * k1 * 4, kAlign);
+    pl.off_ks_items = off;
+    off += round_up(qsa::ks_item_bound(g, b.max_q_len, S) * 16, kAlign);
+    pl.off_ks_hist = off;
+    off += round_up((int64_t)b.n_seqs * qsa::ks_groups(b.max_q_len, S) * (g.nbcap + 1) * 4,
+                    kAlign);
+    pl.off_ks_boff = off;
+    off += round_up((int64_t)b.n_seqs * (g.nbcap + 1) * 4, kAlign);
+    pl.off_ks_po = off;
+    off += round_up(S * g.Hq * k1 * g.D * 2, kAlign);
+    pl.off_ks_pl = off;
+    off += round_up(S * g.Hq * k1 * 4, kAlign);
+  }
   pl.total = T > 0 ? off : 0;
   if ((int64_t)g.T * g.Hkv > 0x7fffffff)
     return fail(QSA_ERR_UNSUPPORTED, "n_tokens * n_kv_heads exceeds the grid limit");
@@ -255,6 +287,27 @@ qsa_status hip_status(hipError_t e, const char* what) {
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// Attention over given selections: the key-stationary path or the others.
+hipError_t attend_launch(const Plan& pl, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* sel, const int32_t* n_blocks, const void* gate, void* out,
+                         void* ws, hipStream_t st) {
+  if (pl.attn.ks) {
+    qsa::KsWork w;
+    w.list = reinterpret_cast<uint32_t*>(ws_at(ws, pl.off_ks_list));
+    w.items = reinterpret_cast<int4*>(ws_at(ws, pl.off_ks_items));
+    w.hist = reinterpret_cast<int32_t*>(ws_at(ws, pl.off_ks_hist));
+    w.boff = reinterpret_cast<int32_t*>(ws_at(ws, pl.off_ks_boff));
+    w.max_q = pl.max_q;
+    w.po = reinterpret_cast<uint16_t*>(ws_at(ws, pl.off_ks_po));
+    w.pl = reinterpret_cast<float*>(ws_at(ws, pl.off_ks_pl));
+    w.sub_tokens = pl.ks_sub;
+    return qsa::launch_attend_ks(pl.geo, w, q, k_cache, v_cache, sel, n_blocks, gate, out, st);
+  }
+  float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
+  return qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, sel, n_blocks, gate,
+                            out, part, st);
+}
 
 // Pointer checks of qsa_forward / qsa_forward_noalloc (everything but the workspace).
 qsa_status check_forward_args(const Plan& pl, const void* q, const void* k_new,
@@ -407,10 +460,8 @@ qsa_status qsa_attend(const qsa_params* params, const qsa_batch* batch, const vo
     QSA_TRY(need(n_blocks, "n_blocks", 4));
   }
   QSA_TRY(check_ws(pl, ws, ws_bytes));
-  float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
-  return hip_status(qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, sel,
-                                       n_blocks, gate, out, part,
-                                       static_cast<hipStream_t>(stream)),
+  return hip_status(attend_launch(pl, q, k_cache, v_cache, sel, n_blocks, gate, out, ws,
+                                  static_cast<hipStream_t>(stream)),
                     "attend launch");
 }
 
@@ -491,8 +542,8 @@ qsa_status forward_launch(const Plan& pl, const qsa_batch* batch, const void* q,
   }
   // Decode attention with few candidate blocks makes the selection itself
   // (no separate select launch); otherwise select, then attend.
-  const bool fused = qsa_layer && !pl.attn.mfma && pl.elem == qsa::kBF16 && pl.geo.D == 128 &&
-                     pl.geo.nbcap <= qsa::kSelectInKernelMaxBlocks;
+  const bool fused = qsa_layer && !pl.attn.mfma && !pl.attn.ks && pl.elem == qsa::kBF16 &&
+                     pl.geo.D == 128 && pl.geo.nbcap <= qsa::kSelectInKernelMaxBlocks;
   float* part = reinterpret_cast<float*>(ws_at(ws, pl.off_part));
   if (fused) {
     const qsa::InKernelSelect fs = {reinterpret_cast<const float*>(ws_at(ws, pl.off_scores)), sel,
@@ -505,8 +556,7 @@ qsa_status forward_launch(const Plan& pl, const qsa_batch* batch, const void* q,
     float* scores = reinterpret_cast<float*>(ws_at(ws, pl.off_scores));
     QSA_TRY(hip_status(qsa::launch_select(pl.geo, scores, sel, nblk, st), "select launch"));
   }
-  return hip_status(qsa::launch_attend(pl.geo, pl.elem, pl.attn, q, k_cache, v_cache, sel, nblk,
-                                       gate, out, part, st),
+  return hip_status(attend_launch(pl, q, k_cache, v_cache, sel, nblk, gate, out, ws, st),
                     "attend launch");
 }
 
@@ -656,9 +706,10 @@ qsa_status qsa_block_forward(const qsa_params* params, const qsa_block_params* b
 #ifdef QSA_COUNT_KEYS
 // Debug builds only (include/qsa_probe.h).
 int64_t qsa_probe_keys_visited(int32_t reset) {
-  unsigned long long v = 0;
+  unsigned long long v = 0, w = 0;
   if (qsa::keys_visited(&v, reset != 0) != hipSuccess) return -1;
-  return (int64_t)v;
+  if (qsa::ks_keys_visited(&w, reset != 0) != hipSuccess) return -1;
+  return (int64_t)(v + w);
 }
 #endif
 

@@ -44,6 +44,7 @@ struct RopeTab {
 
 // Split-KV plan of the attention kernels.
 struct AttnPlan {
+  int32_t ks;            // 1: key-stationary prefill path (launch_attend_ks)
   int32_t mfma;          // 1: prefill MFMA kernel (one wave per unit, no splits)
   int32_t n_splits;      // splits per (token, KV head), <= kPlanMaxSplits
   int32_t tiles;         // 64-token tiles of the longest selection list
@@ -125,5 +126,50 @@ hipError_t keys_visited(unsigned long long* value, bool reset);
 
 // True when a kernel instantiation exists for G heads per KV head and dim D.
 bool attend_supported(int G, int D);
+
+// Key-stationary prefill attention (qsa_prefill_ks.hip): per sub-batch of
+// queries, a plan launch sorts the selection entries by block, an attention
+// launch runs each block's queries through the block's K/V once, and a merge
+// launch combines each query's per-block partial states.
+constexpr int kKsSlotBits = 12;       // an entry packs (query << 12 | slot): k + 1 <= 4096
+constexpr int kKsMaxBlocks = 8192;    // candidate blocks + 1 that one plan workgroup holds
+constexpr int kKsMinQueries = 512;    // new tokens of one sequence that make the path pay
+constexpr int kKsSubTokens = 4096;    // queries per sub-batch (bounds the partial buffers)
+constexpr int kKsItemMax = 128;       // queries per work item of the attention
+constexpr int kKsMaxSlots = 128;      // k + 1 the path takes
+struct KsArgs {
+  int32_t t_lo, t_hi;    // the sub-batch's queries [t_lo, t_hi)
+  int32_t k1, nb1;       // slots per query (k + 1: the tail is slot k); blocks + 1
+  int32_t item_tokens;   // queries per work item
+  int32_t ng;            // counting groups per sequence
+  int32_t nr;            // query ranges per sequence (of the work-item order)
+  int32_t n_items;       // work-item slots of this sub-batch
+  uint32_t* list;        // [sub * k1] entries, grouped by block
+  int32_t* hist;         // [B][ng][nb1] entries per (group, block)
+  int32_t* boff;         // [B][nb1] first list position of each block
+  int4* items;           // [ks_item_bound] work items {list start, block, count, sequence}
+  uint16_t* po;          // [sub][k1][Hq][D] bf16 partial outputs, normalised
+  float* pl;             // [sub][k1][Hq] base-2 log-sum-exp of each partial
+};
+struct KsWork {
+  uint32_t* list;
+  int4* items;
+  int32_t* hist;
+  int32_t* boff;
+  uint16_t* po;
+  float* pl;
+  int32_t sub_tokens;
+  int32_t max_q;         // the batch's longest new-token count
+};
+bool ks_supported(const Geo& g, int elem);
+int ks_item_tokens(const Geo& g);
+int64_t ks_item_bound(const Geo& g, int64_t max_q, int64_t sub_tokens);
+int ks_groups(int64_t max_q, int64_t sub_tokens);
+hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* sel, const int32_t* n_blocks,
+                            const void* gate, void* out, hipStream_t st);
+#ifdef QSA_COUNT_KEYS
+hipError_t ks_keys_visited(unsigned long long* value, bool reset);
+#endif
 
 }  // namespace qsa

@@ -56,51 +56,6 @@ __device__ unsigned long long g_keys_visited;
 
 
 
-// Sequence of token t: the largest b with cu_q[b] <= t (cu_q ascending,
-// cu_q[0] = 0).  The wave reads 64 offsets at a time and counts them with a
-// ballot, so a batch of up to 64 sequences costs one memory round trip
-// instead of a chain of log2(B) dependent loads.  Wave-uniform result.
-__device__ __forceinline__ int seq_of(const int32_t* cu_q, int B, int t) {
-  const int lane = threadIdx.x & 63;
-  int count = 0;
-  for (int b0 = 1; b0 < B; b0 += 64) {
-    const int b = b0 + lane;
-    const bool le = (b < B) && (cu_q[b] <= t);
-    const int c = __popcll(__ballot(le));
-    count += c;
-    if (c < 64) break;
-  }
-  return count;
-}
-
-struct QueryPos {
-  int b, p;
-  bool ok;
-};
-// With one new token per sequence, token t is sequence t's token and cu_q[t]
-// = t: one load instead of three dependent ones.
-__device__ __forceinline__ QueryPos query_pos(const Geo& g, int t) {
-  QueryPos q;
-  if (g.one_q) {
-    q.b = t;
-    q.p = g.past_len[t];
-  } else {
-    q.b = seq_of(g.cu_q, g.B, t);
-    q.p = g.past_len[q.b] + (t - g.cu_q[q.b]);
-  }
-  q.ok = q.p >= 0 && q.p < g.cap;
-  return q;
-}
-
-// Element offset of row s of (sequence b, KV head kvh) in a K or V cache, or -1
-// when the row is outside the stated capacity / page pool.
-__device__ __forceinline__ int64_t kv_row(const Geo& g, int b, int kvh, int s) {
-  if (s < 0 || s >= g.cap) return -1;
-  if (g.page_table == nullptr) return ((int64_t)(b * g.Hkv + kvh) * g.cap + s) * g.D;
-  const int page = g.page_table[(int64_t)b * g.max_pages + (s >> g.log2ps)];
-  if (page < 0 || page >= g.n_pages) return -1;
-  return (((int64_t)page * g.Hkv + kvh) * g.page_size + (s & (g.page_size - 1))) * g.D;
-}
 // Element offset of row s of sequence b in the indexer-key cache, or -1.
 __device__ __forceinline__ int64_t idx_row(const Geo& g, int b, int s) {
   if (s < 0 || s >= g.cap) return -1;

@@ -1,0 +1,645 @@
+// Key-stationary prefill attention for gfx950 (bf16, D = 128).
+//
+// In a prefill chunk every query picks its own k blocks (plus its tail), but
+// all of them pick from the same few hundred candidate blocks, so each block
+// is picked by hundreds of the chunk's queries.  A per-query kernel gathers
+// every picked block once per query (8 flop per byte gathered); this path
+// turns the selection around instead:
+//
+//   ks_count, ks_scan, ks_scatter   the plan: per sequence, a counting sort
+//              of the (query, slot) entries of the selection (and each
+//              query's tail) by block: the block's list of queries, cut into
+//              work items of up to kKsItemMax queries.
+//   ks_attn    one workgroup per (item, KV head): the block's K and V rows go
+//              to LDS once; the item's queries run through it 64 (query,
+//              head) rows at a time as dense bf16 MFMA tiles, S^T = K Q^T
+//              then O^T = V^T P^T, with a causal mask per row (the tail block
+//              of a query is partial).  Each row's partial state is stored:
+//              its output normalised by its own sum (bf16) and its base-2
+//              log-sum-exp (fp32), at (query, slot, head).
+//   ks_merge   per (query, 16 heads), the log-sum-exp merge of the query's
+//              slots (its selected blocks, then the tail), then the sigmoid
+//              gate.
+//
+// The attention is the one of the pages' QSA description (MTPLX "Native
+// Backend Components", section "Qwen Sparse Attention": standard gated GQA
+// over the per-query selection intersected with the causal mask); the merge
+// is the online-softmax state combination that "Porting Qwen4 to llama.cpp",
+// section "CUDA Optimization Should Follow State Correctness", names for the
+// direct indexed consumer.  Results do not depend on how queries are grouped
+// into tiles: every output row of a matrix-core product depends on its own
+// row only.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+#include "qsa_device.h"
+
+#ifdef QSA_COUNT_KEYS
+// Debug builds: (query, K/V row) pairs attended, per KV head.
+__device__ unsigned long long g_ks_keys_visited;
+#endif
+
+// Two fp32 values -> a bf16 pair (low, high), round to nearest even by the
+// hardware conversion.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+constexpr int kRows = 64;    // (query, head) rows per tile of ks_attn (4 waves x 16)
+constexpr int kGroup = 64;   // queries per counting group of the plan
+constexpr int kRangeGroups = 16;  // groups per query range of the work-item order
+constexpr int kScanThreads = 1024;
+
+// Entries of a block's query list: the query's index in the call and its slot
+// (position in its selection, or k for the tail), packed as t << 12 | slot.
+__device__ __forceinline__ uint32_t pack_entry(int t, int slot) {
+  return ((uint32_t)t << kKsSlotBits) | (uint32_t)slot;
+}
+
+// Sequence b's queries inside this sub-batch [t_lo, t_hi).
+struct SeqRange {
+  int t0, t1;  // global token indices, t0 <= t1
+};
+__device__ __forceinline__ SeqRange seq_range(const Geo& g, const KsArgs& a, int b) {
+  SeqRange s;
+  s.t0 = min(max(g.cu_q[b], a.t_lo), a.t_hi);
+  s.t1 = min(max(g.cu_q[b + 1], a.t_lo), a.t_hi);
+  return s;
+}
+// First work item of sequence b's region (the host sizes the item table with
+// the same bound: ks_item_bound).
+__device__ __forceinline__ int item_base(const KsArgs& a, int b, int t_rel) {
+  return (int)(((int64_t)t_rel * a.k1) / a.item_tokens) + b * (a.nr * a.nb1 + 1);
+}
+
+// Block of entry (query t at position p = past + t - cu0, slot): the
+// selection entry (slots below the query's n_blocks), or the query's tail
+// block (slot k, when the tail is not empty); -1 when there is none.
+__device__ __forceinline__ int entry_block(const Geo& g, const KsArgs& a,
+                                           const int32_t* __restrict__ sel,
+                                           const int32_t* __restrict__ nblk, int p, int t,
+                                           int slot) {
+  if (p < 0 || p >= g.cap) return -1;
+  const int n = p + 1, nb = n >> g.log2r;
+  if (slot == g.k) return (n > (nb << g.log2r) && nb < a.nb1) ? nb : -1;
+  const int nk = max(0, min(nblk[t], min(g.k, nb)));
+  if (slot >= nk) return -1;
+  const int j = sel[(int64_t)t * g.k + slot];
+  return (j >= 0 && j < nb && j < a.nb1) ? j : -1;
+}
+
+// Plan, step 1: grid (query group, sequence).  Entries per block of the
+// group's kGroup queries, counted in LDS and stored as the group's row of
+// the histogram.
+__global__ __launch_bounds__(256) void ks_count_kernel(Geo g, KsArgs a,
+                                                      const int32_t* __restrict__ sel,
+                                                      const int32_t* __restrict__ nblk) {
+  extern __shared__ int32_t hist_lds[];
+  const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqRange sr = seq_range(g, a, b);
+  const int ta = min(sr.t0 + gi * kGroup, sr.t1), tb = min(sr.t1, ta + kGroup);
+  const int past = g.past_len[b], cu0 = g.cu_q[b], K1 = a.k1;
+  for (int i = tid; i < a.nb1; i += 256) hist_lds[i] = 0;
+  __syncthreads();
+  for (int e = tid; e < (tb - ta) * K1; e += 256) {
+    const int t = ta + e / K1, slot = e - (e / K1) * K1;
+    const int j = entry_block(g, a, sel, nblk, past + (t - cu0), t, slot);
+    if (j >= 0) atomicAdd(&hist_lds[j], 1);
+  }
+  __syncthreads();
+  int32_t* row = a.hist + ((int64_t)b * a.ng + gi) * a.nb1;
+  for (int i = tid; i < a.nb1; i += 256) row[i] = hist_lds[i];
+}
+
+// Block-wide exclusive scan of one int per thread (kScanThreads threads).
+__device__ __forceinline__ int scan_excl(int v, int* total, int* sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) sh[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < kScanThreads / 64 ? sh[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kScanThreads / 64; d <<= 1) {
+      const int y = __shfl_up(w, d, 64);
+      if (lane >= d) w += y;
+    }
+    if (lane < kScanThreads / 64) sh[lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  const int before = wid > 0 ? sh[wid - 1] : 0;
+  *total = sh[kScanThreads / 64 - 1];
+  __syncthreads();  // sh is reused by the next scan
+  return before + x - v;
+}
+
+// Plan, step 2: one workgroup per sequence.  Per block: the total over the
+// groups and the block's first list position (blocks ascending; inside a
+// block, groups in order).  Work items are cut per (query range of
+// kRangeGroups groups, block), ranges outermost: items dispatched together
+// then read the queries of one range, which stay in the L2 of their XCD.
+// Unused item slots of the sequence's region are written empty.
+__global__ __launch_bounds__(kScanThreads) void ks_scan_kernel(Geo g, KsArgs a) {
+  __shared__ int sh[kScanThreads / 64];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const SeqRange sr = seq_range(g, a, b);
+  const int NB1 = a.nb1, ng = a.ng;
+  const int32_t* rows = a.hist + (int64_t)b * ng * NB1;
+  constexpr int PER = kKsMaxBlocks / kScanThreads;
+  const int j0 = tid * PER;
+  // per (range, block) counts, one range at a time
+  auto range_counts = [&](int r, int (&c)[PER]) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) c[i] = 0;
+    if (j0 >= NB1) return;
+    const int g1 = min(ng, (r + 1) * kRangeGroups);
+    constexpr int GB = 8;  // group rows loaded together
+#pragma unroll 1
+    for (int x0 = 0; x0 < kRangeGroups; x0 += GB) {
+      int v[GB][PER];
+#pragma unroll
+      for (int x = 0; x < GB; ++x)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int gi = r * kRangeGroups + x0 + x;
+          v[x][i] = (gi < g1 && j0 + i < NB1) ? rows[(int64_t)gi * NB1 + j0 + i] : 0;
+        }
+#pragma unroll
+      for (int x = 0; x < GB; ++x)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) c[i] += v[x][i];
+    }
+  };
+  const int n_ranges = (ng + kRangeGroups - 1) / kRangeGroups;
+  int tot[PER], ents = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) tot[i] = 0;
+  for (int r = 0; r < n_ranges; ++r) {
+    int c[PER];
+    range_counts(r, c);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) tot[i] += c[i];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) ents += tot[i];
+  int total_ents;
+  const int ent_before = scan_excl(ents, &total_ents, sh);
+  const int list0 = (sr.t0 - a.t_lo) * a.k1;  // the sequence's list region
+  int32_t* boff = a.boff + (int64_t)b * NB1;
+  int pos[PER];  // list position of each block's next range
+  {
+    int o = list0 + ent_before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (j0 + i < NB1) boff[j0 + i] = o;
+      pos[i] = o;
+      o += tot[i];
+    }
+  }
+  const int base = item_base(a, b, sr.t0 - a.t_lo);
+  const int base_next = item_base(a, b + 1, sr.t1 - a.t_lo);
+  int it0 = base;
+  for (int r = 0; r < n_ranges; ++r) {
+    int c[PER], items = 0;
+    range_counts(r, c);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) items += (c[i] + a.item_tokens - 1) / a.item_tokens;
+    int total_items;
+    int it = it0 + scan_excl(items, &total_items, sh);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      for (int x = 0; x < c[i]; x += a.item_tokens, ++it)
+        a.items[it] = make_int4(pos[i] + x, j0 + i, min(a.item_tokens, c[i] - x), b);
+      pos[i] += c[i];
+    }
+    it0 += total_items;
+  }
+  for (int x = it0 + tid; x < base_next; x += kScanThreads) a.items[x] = make_int4(0, 0, 0, b);
+}
+
+// Plan, step 3: grid (query group, sequence).  Each entry goes to its
+// block's list at the block's first position, plus the entries of the
+// block from earlier groups, plus its rank among this group's entries of
+// the block.
+__global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
+                                                        const int32_t* __restrict__ sel,
+                                                        const int32_t* __restrict__ nblk) {
+  extern __shared__ int32_t pos_lds[];
+  constexpr int GB = 16;
+  const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqRange sr = seq_range(g, a, b);
+  const int ta = min(sr.t0 + gi * kGroup, sr.t1), tb = min(sr.t1, ta + kGroup);
+  if (ta >= tb) return;
+  const int past = g.past_len[b], cu0 = g.cu_q[b], K1 = a.k1, NB1 = a.nb1;
+  const int32_t* rows = a.hist + (int64_t)b * a.ng * NB1;
+  const int32_t* boff = a.boff + (int64_t)b * NB1;
+  for (int j = tid; j < NB1; j += 256) {
+    int acc = boff[j];
+    for (int g0 = 0; g0 < gi; g0 += GB) {
+      int v[GB];
+#pragma unroll
+      for (int x = 0; x < GB; ++x) v[x] = g0 + x < gi ? rows[(int64_t)(g0 + x) * NB1 + j] : 0;
+#pragma unroll
+      for (int x = 0; x < GB; ++x) acc += v[x];
+    }
+    pos_lds[j] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < (tb - ta) * K1; e += 256) {
+    const int t = ta + e / K1, slot = e - (e / K1) * K1;
+    const int j = entry_block(g, a, sel, nblk, past + (t - cu0), t, slot);
+    if (j >= 0) a.list[atomicAdd(&pos_lds[j], 1)] = pack_entry(t, slot);
+  }
+}
+
+// One workgroup (4 waves) per (work item, KV head).  Matrix-core layout of
+// v_mfma_f32_16x16x32_bf16 (l = lane, c16 = l % 16, grp = l / 16):
+//   A[i][k]: i = c16, k = 8 grp + e;  B[k][j]: j = c16, k = 8 grp + e;
+//   C[i][j]: j = c16, i = 4 grp + r.
+// The item's queries run through the block 64 (query, head) rows at a
+// time; wave w holds rows 16 w .. 16 w + 15 of each tile (row R = query R / G
+// of the tile, head R % G), lane c16 row 16 w + c16.
+//   S^T[key][row] = K (A: key 16 n + c16 from LDS, 272-byte rows) x Q^T
+//     (B: the row's query, 16 bytes from memory, the next tile's requested
+//     during this one): a lane holds row c16's scores of keys 16 n + 4 grp + r;
+//   the row's softmax over the block's keys it may see (causal mask), in
+//     base 2: in-lane over 4 KT keys, then two row swaps; p rounded to bf16;
+//   O^T[dim][row] = V^T (A: a dim's 8 keys through two transposing LDS reads
+//     of the 288-byte V rows) x P^T (B: p straight from the softmax
+//     registers; key order inside a 32-key step follows the accumulator
+//     layout, and V follows it): with V's dims placed as below, a lane holds
+//     row c16's dims 32 m + 8 grp .. +7 in tiles 2 m and 2 m + 1, stored as
+//     16 bytes.
+template <int G, int KT>
+__global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
+                                                        const uint16_t* __restrict__ q,
+                                                        const uint16_t* __restrict__ kc,
+                                                        const uint16_t* __restrict__ vc) {
+  constexpr int D = 128, RB = 16 * KT;
+  constexpr int KS = 272, VS = 288;
+  constexpr int TQ = kRows / G;  // queries per tile
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) unsigned char Kl[RB * KS];
+  __shared__ __attribute__((aligned(16))) unsigned char Vl[RB * VS];
+  __shared__ int32_t s_t[kKsItemMax], s_slot[kKsItemMax], s_p[kKsItemMax];
+  // Workgroups go round-robin over the 8 XCDs (blockIdx % 8).  When Hkv
+  // divides 8, XCD x serves KV head x / (8 / Hkv) and items of its residue,
+  // in item order: the items an XCD runs together read one query range.
+  int item_idx, kvh;
+  if (8 % g.Hkv == 0) {
+    const int per = 8 / g.Hkv, x = blockIdx.x & 7;
+    kvh = x / per;
+    item_idx = (blockIdx.x >> 3) * per + (x - kvh * per);
+  } else {
+    item_idx = blockIdx.x / g.Hkv;
+    kvh = blockIdx.x - item_idx * g.Hkv;
+  }
+  if (item_idx >= a.n_items) return;
+  const int4 item = a.items[item_idx];
+  const int cnt = item.z;
+  if (cnt <= 0) return;
+  const int tid = threadIdx.x;
+  const int wid = tid >> 6, lane = tid & 63, c16 = lane & 15, grp = lane >> 4;
+  const int l0 = item.x, j = item.y, b = item.w;
+  const int past = g.past_len[b], cu0 = g.cu_q[b], cu1 = g.cu_q[b + 1];
+  const int n_b = past + (cu1 - cu0);  // rows the sequence holds after this call
+  const int key0 = j << g.log2r;
+  const int h0 = kvh * G;
+
+  if (tid < cnt) {
+    const uint32_t e = a.list[l0 + tid];
+    const int t = (int)(e >> kKsSlotBits);
+    s_t[tid] = t;
+    s_slot[tid] = (int)(e & ((1u << kKsSlotBits) - 1u));
+    s_p[tid] = past + (t - cu0);
+  }
+  // The block's K and V rows to LDS (rows at or past the sequence's length,
+  // or outside the cache, read as zero).
+  for (int cidx = tid; cidx < RB * 16; cidx += 256) {
+    const int row = cidx >> 4, ch = cidx & 15, s = key0 + row;
+    const int64_t off = s < n_b ? kv_row(g, b, kvh, s) : -1;
+    // (unconditional loads at row 0 for rows that read as zero)
+    uint4 kv = *reinterpret_cast<const uint4*>(kc + max(off, (int64_t)0) + 8 * ch);
+    uint4 vv = *reinterpret_cast<const uint4*>(vc + max(off, (int64_t)0) + 8 * ch);
+    if (off < 0) kv = vv = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(Kl + row * KS + 16 * ch) = kv;
+    // V's 4-dim chunks are placed so that the two 16-dim MFMA tiles of each
+    // 32 dims hand a lane 8 consecutive dims of its row: in dims 32 m .. 32 m
+    // + 31, chunk 2 c sits at position c and chunk 2 c + 1 at position 4 + c.
+    unsigned char* vrow = Vl + row * VS + 64 * (ch >> 2) + 8 * (ch & 3);
+    *reinterpret_cast<uint2*>(vrow) = make_uint2(vv.x, vv.y);
+    *reinterpret_cast<uint2*>(vrow + 32) = make_uint2(vv.z, vv.w);
+  }
+  __syncthreads();
+
+  // This lane's row of tile c: its query, slot, position and query vector.
+  const int R = 16 * wid + c16, u = R / G, hh = R - u * G;
+  struct Row {
+    int t, slot, p;
+    uint4 qa[4];
+  };
+  auto load_row = [&](int c, Row& rw) {
+    const int idx = c * TQ + u;
+    rw.t = idx < cnt ? s_t[idx] : -1;
+    rw.slot = idx < cnt ? s_slot[idx] : 0;
+    rw.p = idx < cnt ? s_p[idx] : -1;
+    // (unconditional loads: a row past the item's queries reads query 0's
+    // heads, and its softmax is masked whole)
+    const uint16_t* src = q + ((int64_t)max(rw.t, 0) * g.Hq + h0 + hh) * D + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) rw.qa[ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
+  };
+  const int n_tiles = (cnt + TQ - 1) / TQ;
+  const f32x4_t zero4 = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto run_tile = [&](const Row& rw) {
+#ifdef QSA_COUNT_KEYS
+    if (grp == 0 && rw.t >= 0 && hh == 0)
+      atomicAdd(&g_ks_keys_visited, (unsigned long long)max(0, min(RB, rw.p - key0 + 1)));
+#endif
+    // S^T = K Q^T
+    f32x4_t S[KT];
+#pragma unroll
+    for (int n = 0; n < KT; ++n) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(Kl + (16 * n + c16) * KS + 64 * ks + 16 * grp);
+        S[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ka),
+                                                       __builtin_bit_cast(bf16x8_t, rw.qa[ks]),
+                                                       ks == 0 ? zero4 : S[n], 0, 0, 0);
+      }
+    }
+    // Softmax of row c16 over the keys it may see (the mask only where some
+    // row of the wave cannot see the whole block: its tail block).
+    const int lim = rw.t >= 0 ? rw.p - key0 : -1;  // last visible key of the block
+    float mx = -INFINITY;
+    if (__all(lim >= RB - 1)) {
+#pragma unroll
+      for (int n = 0; n < KT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          S[n][r] *= g.attn_scale_log2;
+          mx = fmaxf(mx, S[n][r]);
+        }
+    } else {
+#pragma unroll
+      for (int n = 0; n < KT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float z = (16 * n + 4 * grp + r <= lim) ? S[n][r] * g.attn_scale_log2 : -INFINITY;
+          S[n][r] = z;
+          mx = fmaxf(mx, z);
+        }
+    }
+    mx = max_xor32(max_xor16(mx));
+    const float mb = mx == -INFINITY ? 0.0f : mx;  // a row with no visible key: every p is 0
+    uint32_t pw[KT][2];
+    float lsum = 0.0f;
+#pragma unroll
+    for (int n = 0; n < KT; ++n)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // exp2(-inf) = 0; the denominator sums the bf16-rounded p
+        const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(S[n][2 * h] - mb),
+                                      __builtin_amdgcn_exp2f(S[n][2 * h + 1] - mb));
+        lsum += bf_lo(pp) + bf_hi(pp);
+        pw[n][h] = pp;
+      }
+    const float l = sum_xor32(sum_xor16(lsum));
+    // O^T = V^T P^T
+    f32x4_t O[8];
+#pragma unroll
+    for (int ks = 0; ks < KT / 2; ++ks) {
+      const unsigned char* v0 = Vl + (32 * ks + 4 * grp + (c16 >> 2)) * VS + 8 * (c16 & 3);
+      const uint4 pb = make_uint4(pw[2 * ks][0], pw[2 * ks][1], pw[2 * ks + 1][0], pw[2 * ks + 1][1]);
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd) {
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(v0 + 32 * nd));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(v0 + 16 * VS + 32 * nd));
+        const uint4 va = make_uint4(__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                    __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y);
+        O[nd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, va),
+                                                        __builtin_bit_cast(bf16x8_t, pb),
+                                                        ks == 0 ? zero4 : O[nd], 0, 0, 0);
+      }
+    }
+    // Partial state of row c16: o / l as bf16 (dims 16 nd + 4 grp .. +3), and
+    // the base-2 log-sum-exp.
+    if (rw.t >= 0) {
+      const int64_t row = ((int64_t)(rw.t - a.t_lo) * a.k1 + rw.slot) * g.Hq + h0 + hh;
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      uint16_t* dst = a.po + row * D + 8 * grp;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t w[4];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const f32x4_t& o = O[2 * m + x];
+          w[2 * x] = pack_bf16(o[0] * inv, o[1] * inv);
+          w[2 * x + 1] = pack_bf16(o[2] * inv, o[3] * inv);
+        }
+        *reinterpret_cast<uint4*>(dst + 32 * m) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      if (grp == 0) a.pl[row] = l > 0.0f ? mx + log2f(l) : -INFINITY;
+    }
+  };
+  // Two row buffers: the loads of tile c + 2 are requested once tile c is
+  // done with its buffer, and arrive while tile c + 1 computes.
+  Row ra, rb;
+  load_row(0, ra);
+  if (n_tiles > 1) load_row(1, rb);
+  for (int c = 0; c < n_tiles; c += 2) {
+    run_tile(ra);
+    if (c + 2 < n_tiles) load_row(c + 2, ra);
+    if (c + 1 >= n_tiles) break;
+    run_tile(rb);
+    if (c + 3 < n_tiles) load_row(c + 3, rb);
+  }
+}
+
+// Log-sum-exp merge of a query's slots, then the gate.  One workgroup per
+// (query, 16 heads); a thread takes 8 consecutive dims of one head (16-byte
+// loads; a slot's 16 heads are 4 KB contiguous).  Slots: the query's
+// selected blocks 0 .. n_blocks-1 (those whose entry names a candidate
+// block: the plan made no entry for the others), then the tail (slot k)
+// when it is not empty.  Every load of a round of kU slots is requested
+// before the first is used; rounds merge under a running maximum.  Queries
+// outside the capacities are left untouched, as the other attention kernels
+// leave them.
+__global__ __launch_bounds__(256) void ks_merge_kernel(Geo g, KsArgs a,
+                                                      const int32_t* __restrict__ sel,
+                                                      const int32_t* __restrict__ nblk,
+                                                      const uint16_t* __restrict__ gate,
+                                                      uint16_t* __restrict__ out) {
+  constexpr int D = 128, kU = 12;
+  const int tl = blockIdx.x, t = a.t_lo + tl;
+  const int h = 16 * blockIdx.y + (threadIdx.x >> 4), d0 = 8 * (threadIdx.x & 15);
+  if (h >= g.Hq) return;
+  const QueryPos qp = query_pos(g, t);
+  if (!qp.ok) return;
+  const int64_t ob = ((int64_t)t * g.Hq + h) * D + d0;
+  const uint4 gw = *reinterpret_cast<const uint4*>(gate + ob);
+  const int n = qp.p + 1, nb = n >> g.log2r;
+  const int nk = max(0, min(nblk[t], min(g.k, nb)));
+  const bool tail = n > (nb << g.log2r);
+  const int64_t row0 = (int64_t)tl * a.k1 * g.Hq + h;  // slot s: row0 + s * Hq
+  const int n_slots = nk + (tail ? 1 : 0);
+  const int32_t* srow = sel + (int64_t)t * g.k;
+  float M = -INFINITY, den = 0.0f;
+  float acc[8];
+#pragma unroll
+  for (int x = 0; x < 8; ++x) acc[x] = 0.0f;
+  for (int i0 = 0; i0 < n_slots; i0 += kU) {
+    float lv[kU];
+    uint4 ov[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(i0 + u, n_slots - 1);
+      const int s = i < nk ? i : g.k;
+      const int jb = i < nk ? srow[i] : 0;
+      const int64_t row = row0 + (int64_t)s * g.Hq;
+      const float lse = a.pl[row];
+      ov[u] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                            reinterpret_cast<const u32x4_t*>(a.po + row * D + d0)));
+      const bool valid = i0 + u < n_slots && (i >= nk || (jb >= 0 && jb < nb));
+      lv[u] = valid ? lse : -INFINITY;
+    }
+    float cm = M;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) cm = fmaxf(cm, lv[u]);
+    const float sc = (M == -INFINITY) ? 0.0f : exp2f(M - cm);
+    den *= sc;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] *= sc;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const float w = lv[u] != -INFINITY ? exp2f(lv[u] - cm) : 0.0f;
+      const uint32_t wv[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
+      den += w;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        acc[2 * x] = fmaf(w, bf_lo(wv[x]), acc[2 * x]);
+        acc[2 * x + 1] = fmaf(w, bf_hi(wv[x]), acc[2 * x + 1]);
+      }
+    }
+    M = cm;
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  const uint32_t gv[4] = {gw.x, gw.y, gw.z, gw.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const float s0 = 1.0f / (1.0f + expf(-bf_lo(gv[x])));
+    const float s1 = 1.0f / (1.0f + expf(-bf_hi(gv[x])));
+    o[x] = (uint32_t)bf16_rne(acc[2 * x] * inv * s0) |
+           ((uint32_t)bf16_rne(acc[2 * x + 1] * inv * s1) << 16);
+  }
+  *reinterpret_cast<uint4*>(out + ob) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+template <int G, int KT>
+void ks_launch_attn(const Geo& g, const KsArgs& a, int n_items, const void* q, const void* kc,
+                    const void* vc, hipStream_t st) {
+  // (8 % Hkv == 0: 8 workgroups per 8 / Hkv items, see the kernel)
+  const int wgs = (8 % g.Hkv == 0) ? 8 * ((n_items + 8 / g.Hkv - 1) / (8 / g.Hkv)) : n_items * g.Hkv;
+  ks_attn_kernel<G, KT><<<wgs, 256, 0, st>>>(
+      g, a, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+      static_cast<const uint16_t*>(vc));
+}
+
+template <int G>
+void ks_launch_g(const Geo& g, const KsArgs& a, int n_items, const void* q, const void* kc,
+                 const void* vc, const int32_t* sel, const int32_t* nblk, const void* gate,
+                 void* out, hipStream_t st) {
+  if (g.r == 32) ks_launch_attn<G, 2>(g, a, n_items, q, kc, vc, st);
+  else if (g.r == 64) ks_launch_attn<G, 4>(g, a, n_items, q, kc, vc, st);
+  else ks_launch_attn<G, 8>(g, a, n_items, q, kc, vc, st);
+  ks_merge_kernel<<<dim3(a.t_hi - a.t_lo, (g.Hq + 15) / 16), 256, 0, st>>>(
+      g, a, sel, nblk, static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out));
+}
+
+}  // namespace
+
+bool ks_supported(const Geo& g, int elem) {
+  return elem == kBF16 && g.D == 128 && !g.kv8 && (g.r == 32 || g.r == 64 || g.r == 128) &&
+         (g.G == 1 || g.G == 2 || g.G == 4 || g.G == 8 || g.G == 16) &&
+         g.k + 1 <= (1 << kKsSlotBits);
+}
+
+int ks_item_tokens(const Geo&) { return kKsItemMax; }
+
+int ks_groups(int64_t max_q, int64_t sub_tokens) {
+  return (int)((std::min(max_q, sub_tokens) + kGroup - 1) / kGroup);
+}
+
+static int ks_ranges(int64_t max_q, int64_t sub_tokens) {
+  return (ks_groups(max_q, sub_tokens) + kRangeGroups - 1) / kRangeGroups;
+}
+
+int64_t ks_item_bound(const Geo& g, int64_t max_q, int64_t sub_tokens) {
+  const int64_t k1 = g.k + 1, nb1 = g.nbcap + 1;
+  return sub_tokens * k1 / ks_item_tokens(g) +
+         (int64_t)g.B * (ks_ranges(max_q, sub_tokens) * nb1 + 1);
+}
+
+hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const void* k_cache,
+                            const void* v_cache, const int32_t* sel, const int32_t* n_blocks,
+                            const void* gate, void* out, hipStream_t st) {
+  if (g.T == 0) return hipSuccess;
+  KsArgs a;
+  a.k1 = g.k + 1;
+  a.nb1 = g.nbcap + 1;
+  a.item_tokens = ks_item_tokens(g);
+  a.ng = ks_groups(w.max_q, w.sub_tokens);
+  a.nr = ks_ranges(w.max_q, w.sub_tokens);
+  a.list = w.list;
+  a.items = w.items;
+  a.hist = w.hist;
+  a.boff = w.boff;
+  a.po = w.po;
+  a.pl = w.pl;
+  const size_t lds = (size_t)a.nb1 * sizeof(int32_t);
+  for (int t_lo = 0; t_lo < g.T; t_lo += w.sub_tokens) {
+    a.t_lo = t_lo;
+    a.t_hi = std::min(g.T, t_lo + w.sub_tokens);
+    const int n_items = (int)ks_item_bound(g, w.max_q, a.t_hi - a.t_lo);
+    a.n_items = n_items;
+    ks_count_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
+    ks_scan_kernel<<<g.B, kScanThreads, 0, st>>>(g, a);
+    ks_scatter_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
+    switch (g.G) {
+      case 1: ks_launch_g<1>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
+      case 2: ks_launch_g<2>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
+      case 4: ks_launch_g<4>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
+      case 8: ks_launch_g<8>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
+      default: ks_launch_g<16>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+#ifdef QSA_COUNT_KEYS
+hipError_t ks_keys_visited(unsigned long long* value, bool reset) {
+  hipError_t e = hipMemcpyFromSymbol(value, HIP_SYMBOL(g_ks_keys_visited), sizeof(*value));
+  if (e != hipSuccess || !reset) return e;
+  const unsigned long long zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_ks_keys_visited), &zero, sizeof(zero));
+}
+#endif
+
+}  // namespace qsa

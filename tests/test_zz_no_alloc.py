@@ -46,7 +46,7 @@ def test_noalloc_matches_forward_on_consecutive_shrinking_calls():
                               ctx_range=(3000, 60000), steps=2)
     small = workloads.make_case("ragged_paged_decode_128k_bf16", n_seqs=3,
                                 ctx_range=(500, 4000), steps=1)
-    prefill = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=2048 + 37, chunk=1024)
+    prefill = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=2048 + 37, chunk=256)
     dc_big = runner.DeviceCase(big, n_layers=2)
     dc_small = runner.DeviceCase(small, n_layers=2)
     dc_pre = runner.DeviceCase(prefill, n_layers=2)
