@@ -153,13 +153,13 @@ __device__ __forceinline__ int scan_excl(int v, int* total, int* sh) {
 // kRangeGroups groups, block), ranges outermost: items dispatched together
 // then read the queries of one range, which stay in the L2 of their XCD.
 // Unused item slots of the sequence's region are written empty.
+template <int PER>  // consecutive blocks per thread (PER * kScanThreads >= nb1)
 __global__ __launch_bounds__(kScanThreads) void ks_scan_kernel(Geo g, KsArgs a) {
   __shared__ int sh[kScanThreads / 64];
   const int b = blockIdx.x, tid = threadIdx.x;
   const SeqRange sr = seq_range(g, a, b);
   const int NB1 = a.nb1, ng = a.ng;
   const int32_t* rows = a.hist + (int64_t)b * ng * NB1;
-  constexpr int PER = kKsMaxBlocks / kScanThreads;
   const int j0 = tid * PER;
   // per (range, block) counts, one range at a time
   auto range_counts = [&](int r, int (&c)[PER]) {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kScanThreads) void ks_scan_kernel(Geo g, KsArgs a) 
     for (int i = 0; i < PER; ++i) c[i] = 0;
     if (j0 >= NB1) return;
     const int g1 = min(ng, (r + 1) * kRangeGroups);
-    constexpr int GB = 8;  // group rows loaded together
+    constexpr int GB = PER >= 8 ? 8 : kRangeGroups;  // group rows loaded together
 #pragma unroll 1
     for (int x0 = 0; x0 < kRangeGroups; x0 += GB) {
       int v[GB][PER];
@@ -384,37 +384,37 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
     }
     // Softmax of row c16 over the keys it may see (the mask only where some
     // row of the wave cannot see the whole block: its tail block).
+    // The maximum is taken over the raw scores (the scale is positive), and
+    // the scale joins the exponent's argument: p = exp2(s c - m c).
     const int lim = rw.t >= 0 ? rw.p - key0 : -1;  // last visible key of the block
+    const float sc = g.attn_scale_log2;
     float mx = -INFINITY;
     if (__all(lim >= RB - 1)) {
 #pragma unroll
       for (int n = 0; n < KT; ++n)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          S[n][r] *= g.attn_scale_log2;
-          mx = fmaxf(mx, S[n][r]);
-        }
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[n][r]);
     } else {
 #pragma unroll
       for (int n = 0; n < KT; ++n)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float z = (16 * n + 4 * grp + r <= lim) ? S[n][r] * g.attn_scale_log2 : -INFINITY;
-          S[n][r] = z;
-          mx = fmaxf(mx, z);
+          if (16 * n + 4 * grp + r > lim) S[n][r] = -INFINITY;
+          mx = fmaxf(mx, S[n][r]);
         }
     }
     mx = max_xor32(max_xor16(mx));
-    const float mb = mx == -INFINITY ? 0.0f : mx;  // a row with no visible key: every p is 0
+    // a row with no visible key: every p is 0 (exp2(-inf) = 0)
+    const float mb = mx == -INFINITY ? 0.0f : mx * sc;
     uint32_t pw[KT][2];
     float lsum = 0.0f;
 #pragma unroll
     for (int n = 0; n < KT; ++n)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        // exp2(-inf) = 0; the denominator sums the bf16-rounded p
-        const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(S[n][2 * h] - mb),
-                                      __builtin_amdgcn_exp2f(S[n][2 * h + 1] - mb));
+        // the denominator sums the bf16-rounded p
+        const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[n][2 * h], sc, -mb)),
+                                      __builtin_amdgcn_exp2f(fmaf(S[n][2 * h + 1], sc, -mb)));
         lsum += bf_lo(pp) + bf_hi(pp);
         pw[n][h] = pp;
       }
@@ -453,9 +453,10 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
           w[2 * x] = pack_bf16(o[0] * inv, o[1] * inv);
           w[2 * x + 1] = pack_bf16(o[2] * inv, o[3] * inv);
         }
-        *reinterpret_cast<uint4*>(dst + 32 * m) = make_uint4(w[0], w[1], w[2], w[3]);
+        __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]},
+                                    reinterpret_cast<u32x4_t*>(dst + 32 * m));
       }
-      if (grp == 0) a.pl[row] = l > 0.0f ? mx + log2f(l) : -INFINITY;
+      if (grp == 0) a.pl[row] = l > 0.0f ? mb + log2f(l) : -INFINITY;
     }
   };
   // Two row buffers: the loads of tile c + 2 are requested once tile c is
@@ -620,7 +621,10 @@ hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const 
     const int n_items = (int)ks_item_bound(g, w.max_q, a.t_hi - a.t_lo);
     a.n_items = n_items;
     ks_count_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
-    ks_scan_kernel<<<g.B, kScanThreads, 0, st>>>(g, a);
+    if (a.nb1 <= kScanThreads) ks_scan_kernel<1><<<g.B, kScanThreads, 0, st>>>(g, a);
+    else if (a.nb1 <= 2 * kScanThreads) ks_scan_kernel<2><<<g.B, kScanThreads, 0, st>>>(g, a);
+    else if (a.nb1 <= 4 * kScanThreads) ks_scan_kernel<4><<<g.B, kScanThreads, 0, st>>>(g, a);
+    else ks_scan_kernel<8><<<g.B, kScanThreads, 0, st>>>(g, a);
     ks_scatter_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
     switch (g.G) {
       case 1: ks_launch_g<1>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
