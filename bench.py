@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB megabytes (counter calibration)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="decode: skip timing the steps replayed from a HIP graph")
     return ap.parse_args()
 
 
@@ -161,12 +163,12 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
-    def fwd(s):
+    def fwd(s, stream_handle=sh):
         l, j = s % L, s // L
         st, x = dc.layers[l], steps_in[s]
         qsa.qsa_forward(dc.params, batches[j], x["q"], x["k_new"], x["v_new"], x["qI"],
                         x["kI_new"], x["w"], x["gate"], st["k"], st["v"], st.get("kI"),
-                        st.get("pooled"), outs[s], sels[s], nbls[s], ws, sh)
+                        st.get("pooled"), outs[s], sels[s], nbls[s], ws, stream_handle)
 
     for s in range(args.warmup):
         fwd(s)
@@ -180,6 +182,17 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     tok_s = T / (ms_step * 1e-3)
     hbm_gbps = per_step / (ms_step * 1e-3) / 1e9
+
+    # The same timed steps captured into one HIP graph and replayed (replays
+    # rewrite the same cache rows with the same values): launch gaps and
+    # host launch cost removed.
+    graph = None
+    if not args.no_graph:
+        graph = graph_timing(torch, lambda: [fwd(s, None) for s in range(args.warmup, total)],
+                             args.steps, stream)
+        if graph is not None:
+            graph["value"] = round(T / (graph["ms_per_step"] * 1e-3), 1)
+            graph["hbm_GBps_step"] = round(per_step / (graph["ms_per_step"] * 1e-3) / 1e9, 1)
 
     # Dominant kernel: the attention of each timed step, launched alone on the
     # same stream in the same layer rotation, bracketed by events.
@@ -214,8 +227,11 @@ def main():
                    else "bf16", "layer_copies": L},
         "hbm_GBps_step": round(hbm_gbps, 1),
         "hbm_frac_step": round(hbm_gbps / HBM_PEAK_GBPS, 4),
+        "graph_replay": graph,
         "step_bytes": {"selected_kv": kv0, "pooled_keys": idx0, "q_gate_out_new_rows": small0},
-        "roofline": {"bound": "hbm", "kernel": "attention (qsa_attend)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("decode attention + split combine as qsa_attend launches them "
+                                "(selection given; in qsa_forward the same kernel also selects)"),
                      "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "avg_launch_us": round(attn_ms * 1e3, 2), "bytes_per_launch": attn_bytes,
@@ -376,6 +392,37 @@ def bench_block_prefill(args, name):
     }), flush=True)
 
 
+def graph_timing(torch, run, steps, stream, replays=3):
+    """Capture run() (the timed steps) into one graph and time replays of it
+    with events on the replay stream: per-step milliseconds, or None when
+    the capture fails."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run()  # warm the capture stream
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        torch.cuda.synchronize()
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        for _ in range(replays):
+            g.replay()
+        b.record(cur)
+        torch.cuda.synchronize()
+        return {"ms_per_step": round(a.elapsed_time(b) / (replays * steps), 5),
+                "replays": replays}
+    except Exception as e:  # noqa: BLE001  (reported, not fatal)
+        log(f"[bench] graph timing failed: {e}")
+        return None
+
+
 def counter_traffic(summary_name):
     """HBM bytes per attention launch from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when the kernel
@@ -446,7 +493,8 @@ def bench_prefill(args, name):
                    "n_q_heads": sp.n_q_heads, "n_kv_heads": sp.n_kv_heads,
                    "head_dim": sp.head_dim, "block_size": r, "budget": sp.budget},
         "selected_gflop_per_step": round(total_flops / 1e9, 2),
-        "roofline": {"bound": "mfma", "kernel": "prefill attention (qsa_attend, bf16 MFMA)",
+        "roofline": {"bound": "mfma", "kernel": ("prefill attention as qsa_attend launches it (key-stationary plan, "
+                                "bf16 MFMA attention, merge)"),
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "avg_launch_us": round(float(np.mean(attn_ms)) * 1e3, 1),
@@ -474,19 +522,38 @@ def cpu_baseline_prefill(case, sp, seconds):
     n = pos + 1
     nb = n // r
     flops = float(((r * np.minimum(k, nb) + n - r * nb) * sp.n_q_heads * 4 * sp.head_dim).sum())
-    reps = 0
-    t0 = time.time()
-    while True:
-        orc.sequence(dims, K, V, kI, pos, case.q[0][pos], case.qI[0][pos], case.w[0][pos],
-                     case.gate[0][pos])
-        reps += 1
-        if time.time() - t0 >= seconds:
-            break
-    dt = time.time() - t0
+    def timed(budget, n_pos):
+        reps = 0
+        t0 = time.time()
+        while True:
+            p = pos[:n_pos]
+            orc.sequence(dims, K, V, kI, p, case.q[0][p], case.qI[0][p], case.w[0][p],
+                         case.gate[0][p])
+            reps += 1
+            if time.time() - t0 >= budget:
+                break
+        return reps, time.time() - t0
+
+    cores = orc.threads()
+    reps, dt = timed(seconds, len(pos))
+    # single core: the same oracle with one OpenMP thread, on 8 of the queries
+    orc.set_threads(1)
+    try:
+        reps1, dt1 = timed(max(2.0, seconds / 3), 8)
+    finally:
+        orc.set_threads(cores)
+    flops8 = float(((r * np.minimum(k, nb[:8]) + n[:8] - r * nb[:8]) * sp.n_q_heads * 4 *
+                    sp.head_dim).sum())
     return {"value": round(reps * flops / dt / 1e12, 5), "unit": "TFLOP/s (selected blocks)",
-            "cores": orc.threads(), "kind": "oracle",
+            "cores": cores, "kind": "oracle",
+            "gflops": round(reps * flops / dt / 1e9, 3),
             "sample": f"{reps} x 64 query tokens of the last 4096-token chunk (OpenMP over "
-                      f"queries), {dt:.1f}s wall", "cpu_model": _cpu_model()}
+                      f"queries), {dt:.1f}s wall",
+            "single_core": {"value": round(reps1 * flops8 / dt1 / 1e12, 6),
+                            "gflops": round(reps1 * flops8 / dt1 / 1e9, 4), "cores": 1,
+                            "sample": f"{reps1} x 8 of those query tokens, one thread, "
+                                      f"{dt1:.1f}s wall"},
+            "cpu_model": _cpu_model()}
 
 
 def cpu_baseline(case, sp, seconds):
@@ -532,6 +599,23 @@ def cpu_baseline(case, sp, seconds):
         orc.sequence(dims, K, V, kI, np.arange(p, p + m), case.q[b][:m], case.qI[b][:m],
                      case.w[b][:m], case.gate[b][:m])
 
+    def step_bytes_of(b):
+        """Algorithmic bytes of sequence b's decode step (selected K/V rows
+        at the oracle's fp32 width counted as the cache's element size,
+        pooled keys): the same formula as the GPU's step bytes."""
+        r_, k_ = sp.block_size, sp.k_blocks
+        tot = 0
+        for i in range(m):
+            n = case.ctx[b] + i + 1
+            if r_ > 0:
+                nb = n // r_
+                nsel = r_ * min(k_, nb) + (n - r_ * nb)
+                tot += nb * sp.idx_dim * 4
+            else:
+                nsel = n
+            tot += nsel * sp.n_kv_heads * sp.head_dim * (1 if sp.kv_fp8 else 2) * 2
+        return tot
+
     threads = min(cores, B)
     reps = 0
     t0 = time.time()
@@ -542,10 +626,31 @@ def cpu_baseline(case, sp, seconds):
             if time.time() - t0 >= seconds:
                 break
     dt = time.time() - t0
+    # single core: one sequence at a time, one OpenMP thread, the first
+    # sequences of the batch
+    omp = orc.threads()
+    orc.set_threads(1)
+    n1, t1 = 0, time.time()
+    try:
+        while True:
+            one(n1 % B)
+            n1 += 1
+            if time.time() - t1 >= max(2.0, seconds / 3):
+                break
+    finally:
+        orc.set_threads(omp)
+    dt1 = time.time() - t1
+    byt1 = sum(step_bytes_of(b) for b in range(B)) * (n1 // B) + \
+        sum(step_bytes_of(b) for b in range(n1 % B))
+    byt = sum(step_bytes_of(b) for b in range(B)) * reps
     return {"value": round(reps * B * m / dt, 2), "unit": "tok/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "GBps": round(byt / dt / 1e9, 3),
             "sample": f"{reps} x one decode step of all {B} sequences ({m} new token(s) "
                       f"each, the same inputs), threads over sequences, {dt:.1f}s wall",
+            "single_core": {"value": round(n1 * m / dt1, 3), "unit": "tok/s", "cores": 1,
+                            "GBps": round(byt1 / dt1 / 1e9, 4),
+                            "sample": f"{n1} sequences' decode steps one after another, one "
+                                      f"thread, {dt1:.1f}s wall"},
             "cpu_model": _cpu_model()}
 
 

@@ -45,6 +45,8 @@ class Oracle:
         L = C.CDLL(path)
         self._L = L
         L.qsa_oracle_threads.restype = C.c_int
+        L.qsa_oracle_set_threads.restype = None
+        L.qsa_oracle_set_threads.argtypes = [C.c_int]
         L.qsa_oracle_pool.restype = C.c_int64
         L.qsa_oracle_pool.argtypes = [C.POINTER(C.c_float), C.c_int64, C.c_int32, C.c_int32,
                                       C.POINTER(C.c_float)]
@@ -92,6 +94,10 @@ class Oracle:
 
     def threads(self) -> int:
         return int(self._L.qsa_oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """OpenMP threads of the calling thread's later oracle calls."""
+        self._L.qsa_oracle_set_threads(int(n))
 
     # --- rotary position embedding ---------------------------------------------
     def rope(self, x, R: int, theta: float, pos) -> np.ndarray:

@@ -64,6 +64,16 @@ int qsa_oracle_threads(void) {
 #endif
 }
 
+/* Threads of the calling thread's later parallel regions (the baseline's
+ * single-core timing); 0 leaves the setting as it is. */
+void qsa_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Mean-pooled indexer key of every complete block ("mean-pooled key blocks",
  * MTPLX page, QSA section).  Column x of block j is the fp32 sum of
  * kI[j*r + s][x] for s = 0..r-1 in ascending order, divided by r.
