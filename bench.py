@@ -488,8 +488,10 @@ def bench_prefill(args, name):
         "unit": "TFLOP/s (selected blocks, whole prefill step)", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded; N(0,1)/sqrt(d); planted blocks at 1% density)",
+        "data": ("synthetic (seeded; N(0,1)/sqrt(d); planted blocks at 1% density" +
+                 ("; K/V cached as E4M3 codes in the Hadamard basis" if sp.kv_fp8 else "") + ")"),
         "config": {"workload": name, "tokens": sp.prefill_len, "chunk": sp.chunk,
+                   "kv_cache": "e4m3+hadamard" if sp.kv_fp8 else "bf16",
                    "n_q_heads": sp.n_q_heads, "n_kv_heads": sp.n_kv_heads,
                    "head_dim": sp.head_dim, "block_size": r, "budget": sp.budget},
         "selected_gflop_per_step": round(total_flops / 1e9, 2),
@@ -517,6 +519,10 @@ def cpu_baseline_prefill(case, sp, seconds):
     K, V, kI = (workloads.as_f32(case.k[0]), workloads.as_f32(case.v[0]),
                 workloads.as_f32(case.kI[0]))
     n_tok = K.shape[0]
+    if sp.kv_fp8:  # the cache as the oracle stores it (outside the timed loop)
+        ks_, vs_ = workloads.kv_scales(sp.head_dim, sp.kv_rotate)
+        Kc = orc.kv8_encode(K, sp.kv_rotate, float(np.float32(1.0) / np.float32(ks_)))
+        Vc = orc.kv8_encode(V, sp.kv_rotate, float(np.float32(1.0) / np.float32(vs_)))
     pos = np.linspace(n_tok - sp.chunk, n_tok - 1, 64).astype(np.int64)
     r, k = sp.block_size, sp.k_blocks
     n = pos + 1
@@ -527,8 +533,12 @@ def cpu_baseline_prefill(case, sp, seconds):
         t0 = time.time()
         while True:
             p = pos[:n_pos]
-            orc.sequence(dims, K, V, kI, p, case.q[0][p], case.qI[0][p], case.w[0][p],
-                         case.gate[0][p])
+            if sp.kv_fp8:
+                orc.sequence_kv8(dims, Kc, Vc, sp.kv_rotate, ks_, vs_, kI, p, case.q[0][p],
+                                 case.qI[0][p], case.w[0][p], case.gate[0][p])
+            else:
+                orc.sequence(dims, K, V, kI, p, case.q[0][p], case.qI[0][p], case.w[0][p],
+                             case.gate[0][p])
             reps += 1
             if time.time() - t0 >= budget:
                 break

@@ -55,7 +55,7 @@ struct Plan {
   int elem;
   size_t off_scores, off_sel, off_nblk, off_part, total;
   // key-stationary prefill (attn.ks): entry lists, work items, partial states
-  size_t off_ks_list, off_ks_items, off_ks_hist, off_ks_boff, off_ks_po, off_ks_pl;
+  size_t off_ks_list, off_ks_items, off_ks_hist, off_ks_boff, off_ks_po, off_ks_pl, off_ks_qrot;
   int32_t ks_sub, max_q;
 };
 
@@ -231,7 +231,7 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
   pl.ks_sub = (int32_t)std::min<int64_t>(std::max<int64_t>(T, 1), qsa::kKsSubTokens);
   pl.max_q = b.max_q_len;
   pl.off_ks_list = pl.off_ks_items = pl.off_ks_hist = pl.off_ks_boff = pl.off_ks_po =
-      pl.off_ks_pl = off;
+      pl.off_ks_pl = pl.off_ks_qrot = off;
   if (pl.attn.ks) {
     const int64_t S = pl.ks_sub, k1 = k + 1;
     pl.off_ks_list = off;
@@ -247,6 +247,8 @@ qsa_status resolve(const qsa_params* P, const qsa_batch* Bt, Plan* out) {
     off += round_up(S * g.Hq * k1 * g.D * 2, kAlign);
     pl.off_ks_pl = off;
     off += round_up(S * g.Hq * k1 * 4, kAlign);
+    pl.off_ks_qrot = off;
+    if (g.rot) off += round_up(S * g.Hq * g.D * 2, kAlign);
   }
   pl.total = T > 0 ? off : 0;
   if ((int64_t)g.T * g.Hkv > 0x7fffffff)
@@ -301,6 +303,7 @@ hipError_t attend_launch(const Plan& pl, const void* q, const void* k_cache, con
     w.max_q = pl.max_q;
     w.po = reinterpret_cast<uint16_t*>(ws_at(ws, pl.off_ks_po));
     w.pl = reinterpret_cast<float*>(ws_at(ws, pl.off_ks_pl));
+    w.qrot = reinterpret_cast<uint16_t*>(ws_at(ws, pl.off_ks_qrot));
     w.sub_tokens = pl.ks_sub;
     return qsa::launch_attend_ks(pl.geo, w, q, k_cache, v_cache, sel, n_blocks, gate, out, st);
   }

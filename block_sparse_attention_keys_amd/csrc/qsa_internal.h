@@ -150,6 +150,7 @@ struct KsArgs {
   int4* items;           // [ks_item_bound] work items {list start, block, count, sequence}
   uint16_t* po;          // [sub][k1][Hq][D] bf16 partial outputs, normalised
   float* pl;             // [sub][k1][Hq] base-2 log-sum-exp of each partial
+  uint16_t* qrot;        // [sub][Hq][D] rotated queries (8-bit rotated caches), else null
 };
 struct KsWork {
   uint32_t* list;
@@ -158,6 +159,7 @@ struct KsWork {
   int32_t* boff;
   uint16_t* po;
   float* pl;
+  uint16_t* qrot;        // [sub][Hq][D] (8-bit rotated caches)
   int32_t sub_tokens;
   int32_t max_q;         // the batch's longest new-token count
 };

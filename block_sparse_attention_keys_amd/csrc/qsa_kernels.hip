@@ -89,14 +89,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float x) {
   return sgn | (uint32_t)((e + 7) * 8 + m - 8);  // m = 16 carries into the exponent
 }
 
-// Walsh-Hadamard butterfly stage across lanes for elements spread over
-// lanes: the partner element sits `dl` lanes away; the element whose index
-// has the stage bit set takes (partner - own), the other (own + partner), as
-// in the in-place transform (x[j], x[j+len]) <- (x[j] + x[j+len], x[j] - x[j+len]).
-__device__ __forceinline__ float fwht_cross(float v, int dl, bool upper) {
-  const float o = __shfl_xor(v, dl, 64);
-  return upper ? (o - v) : (v + o);
-}
 
 // One token's K and V rows (bf16 [Hkv][D], D = 128) into 8-bit caches, one
 // wave: lane l holds elements 2l, 2l+1 of a row; rotated (Sylvester Hadamard,
@@ -129,31 +121,6 @@ __device__ __forceinline__ void store_rows_kv8(const Geo& g, const uint16_t* __r
     const int64_t d = dst(kvh);
     if (d >= 0) *reinterpret_cast<uint16_t*>((which ? vc : kc) + d + 2 * lane) = (uint16_t)c;
   }
-}
-
-// The attention output of one head (D = 128) spread EPT consecutive dims per
-// thread over 128/EPT consecutive lanes of a wave (t_in: the thread's rank
-// among them): with the rotated basis, o = H o' (the 1/D is in out_scale),
-// then the 8-bit storage's output scale.  All lanes of the wave take part.
-template <int EPT>
-__device__ __forceinline__ void kv8_output(const Geo& g, float (&o)[EPT], int t_in) {
-  if (g.rot) {
-#pragma unroll
-    for (int len = 1; len < EPT; len <<= 1)
-#pragma unroll
-      for (int i = 0; i < EPT; ++i)
-        if (!(i & len)) {
-          const float a = o[i], b = o[i + len];
-          o[i] = a + b;
-          o[i + len] = a - b;
-        }
-#pragma unroll
-    for (int dl = 1; dl * EPT < 128; dl <<= 1)
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) o[i] = fwht_cross(o[i], dl, (t_in & dl) != 0);
-  }
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) o[i] *= g.out_scale;
 }
 
 // ---------------------------------------------------------------------------

@@ -266,6 +266,29 @@ __global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
   }
 }
 
+// 8-bit K/V in the rotated basis: each query row of the sub-batch rotated
+// once (q' = H q, the Sylvester Hadamard matrix in the standard butterfly
+// order) and rounded to bf16 for the matrix cores, as the decode kernel does
+// with its staged query.  One wave per (query, head) row: lane l holds dims
+// 2 l, 2 l + 1 (one stage in the lane, six across lanes).
+__global__ __launch_bounds__(256) void ks_rotate_q_kernel(Geo g, KsArgs a,
+                                                         const uint16_t* __restrict__ q) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t - t_lo) * Hq + h
+  if (row >= (int64_t)(a.t_hi - a.t_lo) * g.Hq) return;  // whole wave
+  const uint32_t pr =
+      *reinterpret_cast<const uint32_t*>(q + ((int64_t)a.t_lo * g.Hq + row) * 128 + 2 * lane);
+  const float x = bf_lo(pr), y = bf_hi(pr);
+  float x0 = x + y, x1 = x - y;
+#pragma unroll
+  for (int dl = 1; dl < 64; dl <<= 1) {
+    const bool up = (lane & dl) != 0;
+    x0 = fwht_cross(x0, dl, up);
+    x1 = fwht_cross(x1, dl, up);
+  }
+  *reinterpret_cast<uint32_t*>(a.qrot + row * 128 + 2 * lane) = pack_bf16(x0, x1);
+}
+
 // One workgroup (4 waves) per (work item, KV head).  Matrix-core layout of
 // v_mfma_f32_16x16x32_bf16 (l = lane, c16 = l % 16, grp = l / 16):
 //   A[i][k]: i = c16, k = 8 grp + e;  B[k][j]: j = c16, k = 8 grp + e;
@@ -284,7 +307,10 @@ __global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
 //     layout, and V follows it): with V's dims placed as below, a lane holds
 //     row c16's dims 32 m + 8 grp .. +7 in tiles 2 m and 2 m + 1, stored as
 //     16 bytes.
-template <int G, int KT>
+// KV8: the caches hold E4M3 codes (one byte per element), turned into bf16
+// (exactly) as they go to LDS; the scales and the rotation are in the
+// softmax scale, the rotated query (ks_rotate_q_kernel) and the merge.
+template <int G, int KT, bool KV8>
 __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
                                                         const uint16_t* __restrict__ q,
                                                         const uint16_t* __restrict__ kc,
@@ -329,6 +355,36 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
   }
   // The block's K and V rows to LDS (rows at or past the sequence's length,
   // or outside the cache, read as zero).
+  if constexpr (KV8) {
+    const uint8_t* k8 = reinterpret_cast<const uint8_t*>(kc);
+    const uint8_t* v8 = reinterpret_cast<const uint8_t*>(vc);
+    for (int cidx = tid; cidx < RB * 8; cidx += 256) {
+      const int row = cidx >> 3, c8 = cidx & 7, s = key0 + row;  // dims 16 c8 .. +15
+      const int64_t off = s < n_b ? kv_row(g, b, kvh, s) : -1;
+      uint4 kw = *reinterpret_cast<const uint4*>(k8 + max(off, (int64_t)0) + 16 * c8);
+      uint4 vw = *reinterpret_cast<const uint4*>(v8 + max(off, (int64_t)0) + 16 * c8);
+      if (off < 0) kw = vw = make_uint4(0u, 0u, 0u, 0u);
+      uint32_t kb[8], vb[8];
+      const uint32_t kx[4] = {kw.x, kw.y, kw.z, kw.w}, vx[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kb[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kx[i], 1.0f, false));
+        kb[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kx[i], 1.0f, true));
+        vb[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vx[i], 1.0f, false));
+        vb[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vx[i], 1.0f, true));
+      }
+      *reinterpret_cast<uint4*>(Kl + row * KS + 32 * c8) = make_uint4(kb[0], kb[1], kb[2], kb[3]);
+      *reinterpret_cast<uint4*>(Kl + row * KS + 32 * c8 + 16) = make_uint4(kb[4], kb[5], kb[6], kb[7]);
+      // V: 4-dim chunks 4 (c8 % 2) + i of the 32-dim group c8 / 2, placed as
+      // below (chunk 2 c at position c, chunk 2 c + 1 at position 4 + c)
+      unsigned char* vrow = Vl + row * VS + 64 * (c8 >> 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int cc = 4 * (c8 & 1) + i, pos = (cc & 1) ? 4 + (cc >> 1) : (cc >> 1);
+        *reinterpret_cast<uint2*>(vrow + 8 * pos) = make_uint2(vb[2 * i], vb[2 * i + 1]);
+      }
+    }
+  } else
   for (int cidx = tid; cidx < RB * 16; cidx += 256) {
     const int row = cidx >> 4, ch = cidx & 15, s = key0 + row;
     const int64_t off = s < n_b ? kv_row(g, b, kvh, s) : -1;
@@ -359,7 +415,10 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
     rw.p = idx < cnt ? s_p[idx] : -1;
     // (unconditional loads: a row past the item's queries reads query 0's
     // heads, and its softmax is masked whole)
-    const uint16_t* src = q + ((int64_t)max(rw.t, 0) * g.Hq + h0 + hh) * D + 8 * grp;
+    const uint16_t* src =
+        a.qrot != nullptr
+            ? a.qrot + ((int64_t)(max(rw.t, a.t_lo) - a.t_lo) * g.Hq + h0 + hh) * D + 8 * grp
+            : q + ((int64_t)max(rw.t, 0) * g.Hq + h0 + hh) * D + 8 * grp;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) rw.qa[ks] = *reinterpret_cast<const uint4*>(src + 32 * ks);
   };
@@ -541,24 +600,28 @@ __global__ __launch_bounds__(256) void ks_merge_kernel(Geo g, KsArgs a,
     M = cm;
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) acc[x] *= inv;
+  // 8-bit storage: the head's 16 threads un-rotate and scale the output
+  // (every thread of a head is present: heads are whole 16-lane groups)
+  if (g.kv8) kv8_output(g, acc, threadIdx.x & 15);
   const uint32_t gv[4] = {gw.x, gw.y, gw.z, gw.w};
   uint32_t o[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const float s0 = 1.0f / (1.0f + expf(-bf_lo(gv[x])));
     const float s1 = 1.0f / (1.0f + expf(-bf_hi(gv[x])));
-    o[x] = (uint32_t)bf16_rne(acc[2 * x] * inv * s0) |
-           ((uint32_t)bf16_rne(acc[2 * x + 1] * inv * s1) << 16);
+    o[x] = (uint32_t)bf16_rne(acc[2 * x] * s0) | ((uint32_t)bf16_rne(acc[2 * x + 1] * s1) << 16);
   }
   *reinterpret_cast<uint4*>(out + ob) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-template <int G, int KT>
+template <int G, int KT, bool KV8>
 void ks_launch_attn(const Geo& g, const KsArgs& a, int n_items, const void* q, const void* kc,
                     const void* vc, hipStream_t st) {
   // (8 % Hkv == 0: 8 workgroups per 8 / Hkv items, see the kernel)
   const int wgs = (8 % g.Hkv == 0) ? 8 * ((n_items + 8 / g.Hkv - 1) / (8 / g.Hkv)) : n_items * g.Hkv;
-  ks_attn_kernel<G, KT><<<wgs, 256, 0, st>>>(
+  ks_attn_kernel<G, KT, KV8><<<wgs, 256, 0, st>>>(
       g, a, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
       static_cast<const uint16_t*>(vc));
 }
@@ -567,9 +630,15 @@ template <int G>
 void ks_launch_g(const Geo& g, const KsArgs& a, int n_items, const void* q, const void* kc,
                  const void* vc, const int32_t* sel, const int32_t* nblk, const void* gate,
                  void* out, hipStream_t st) {
-  if (g.r == 32) ks_launch_attn<G, 2>(g, a, n_items, q, kc, vc, st);
-  else if (g.r == 64) ks_launch_attn<G, 4>(g, a, n_items, q, kc, vc, st);
-  else ks_launch_attn<G, 8>(g, a, n_items, q, kc, vc, st);
+  if (g.kv8) {
+    if (g.r == 32) ks_launch_attn<G, 2, true>(g, a, n_items, q, kc, vc, st);
+    else if (g.r == 64) ks_launch_attn<G, 4, true>(g, a, n_items, q, kc, vc, st);
+    else ks_launch_attn<G, 8, true>(g, a, n_items, q, kc, vc, st);
+  } else {
+    if (g.r == 32) ks_launch_attn<G, 2, false>(g, a, n_items, q, kc, vc, st);
+    else if (g.r == 64) ks_launch_attn<G, 4, false>(g, a, n_items, q, kc, vc, st);
+    else ks_launch_attn<G, 8, false>(g, a, n_items, q, kc, vc, st);
+  }
   ks_merge_kernel<<<dim3(a.t_hi - a.t_lo, (g.Hq + 15) / 16), 256, 0, st>>>(
       g, a, sel, nblk, static_cast<const uint16_t*>(gate), static_cast<uint16_t*>(out));
 }
@@ -577,7 +646,7 @@ void ks_launch_g(const Geo& g, const KsArgs& a, int n_items, const void* q, cons
 }  // namespace
 
 bool ks_supported(const Geo& g, int elem) {
-  return elem == kBF16 && g.D == 128 && !g.kv8 && (g.r == 32 || g.r == 64 || g.r == 128) &&
+  return elem == kBF16 && g.D == 128 && (g.r == 32 || g.r == 64 || g.r == 128) &&
          (g.G == 1 || g.G == 2 || g.G == 4 || g.G == 8 || g.G == 16) &&
          g.k + 1 <= (1 << kKsSlotBits);
 }
@@ -614,12 +683,16 @@ hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const 
   a.boff = w.boff;
   a.po = w.po;
   a.pl = w.pl;
+  a.qrot = g.rot ? w.qrot : nullptr;
   const size_t lds = (size_t)a.nb1 * sizeof(int32_t);
   for (int t_lo = 0; t_lo < g.T; t_lo += w.sub_tokens) {
     a.t_lo = t_lo;
     a.t_hi = std::min(g.T, t_lo + w.sub_tokens);
     const int n_items = (int)ks_item_bound(g, w.max_q, a.t_hi - a.t_lo);
     a.n_items = n_items;
+    if (a.qrot != nullptr)
+      ks_rotate_q_kernel<<<(int)(((int64_t)(a.t_hi - a.t_lo) * g.Hq + 3) / 4), 256, 0, st>>>(
+          g, a, static_cast<const uint16_t*>(q));
     ks_count_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
     if (a.nb1 <= kScanThreads) ks_scan_kernel<1><<<g.B, kScanThreads, 0, st>>>(g, a);
     else if (a.nb1 <= 2 * kScanThreads) ks_scan_kernel<2><<<g.B, kScanThreads, 0, st>>>(g, a);

@@ -131,6 +131,12 @@ SPECS: Dict[str, Spec] = {
         n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,
         block_size=64, budget=4096, ctx_lo=8192, ctx_hi=131072, steps=1,
         page_size=64, kv_fp8=True, kv_rotate=True),
+    # The 32K chunked prefill over the 8-bit rotated K/V cache.
+    "chunked_prefill_32k_fp8kv": Spec(
+        name="chunked_prefill_32k_fp8kv", kind="prefill", dtype=BF16, n_seqs=1,
+        n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,
+        block_size=64, budget=2048, prefill_len=32768, chunk=4096,
+        planted_density=0.01, kv_fp8=True, kv_rotate=True),
     "mtp_dense_ragged_bf16": Spec(
         name="mtp_dense_ragged_bf16", kind="decode", dtype=BF16, n_seqs=32,
         n_q_heads=16, n_kv_heads=2, head_dim=128, n_idx_heads=4, idx_dim=64,

@@ -88,10 +88,28 @@ def test_dense_layer_rotated():
 
 
 def test_chunked_prefill_rotated():
-    """Chunked prefill: each chunk stores its rows and attends them in the same call."""
+    """Chunked prefill: each chunk stores its rows and attends them in the same
+    call (chunks of 700 tokens: the key-stationary path, codes turned into
+    bf16 on their way to LDS, the rotated query, the merge un-rotating)."""
     case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=2048 + 45, chunk=700)
     dc, seqf = _run(case, True)
     _codes_equal(dc, seqf)
+
+
+def test_chunked_prefill_unrotated_and_short_chunks():
+    """The 8-bit cache without the rotation through the key-stationary path,
+    and short chunks (the split-list kernel)."""
+    case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=1500 + 13, chunk=600)
+    dc, seqf = _run(case, False)
+    _codes_equal(dc, seqf)
+    case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=700, chunk=200)
+    _run(case, True)
+
+
+def test_chunked_prefill_32k_full_sampled():
+    """The full 32K chunked prefill over the rotated 8-bit cache, 48 sampled
+    queries per 4096-token chunk."""
+    _run(workloads.make_case("chunked_prefill_32k_fp8kv"), True, sample=48)
 
 
 def test_saturating_scales():
