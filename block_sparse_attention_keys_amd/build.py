@@ -62,6 +62,52 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     return out
 
 
+# Host AddressSanitizer build of the C-ABI layer (host code only; the device
+# code is built as usual): for the CPU tests that drive argument validation
+# under ASan.  Load it with the compiler's ASan runtime preloaded.
+ASAN_LIB = os.path.join(PKG, "_build", "asan", "libqsa_asan.so")
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_asan() -> str:
+    """libqsa_asan.so: qsa_api.hip with host ASan, the kernels' objects as
+    built for the product library (built first if missing)."""
+    hipcc = _hipcc()
+    lib_dir = os.path.join(PKG, "_build", "lib")
+    objs = [os.path.join(lib_dir, os.path.splitext(x)[0] + ".o") for x in SOURCES
+            if x != "qsa_api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build(LIB)
+    adir = os.path.dirname(ASAN_LIB)
+    os.makedirs(adir, exist_ok=True)
+    api = os.path.join(adir, "qsa_api.o")
+    cmd = [hipcc, *FLAGS, *ASAN_FLAGS, "-c", os.path.join(CSRC, "qsa_api.hip"), "-o", api]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the ASan build:\n{p.stderr}")
+    tmp = ASAN_LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *ASAN_FLAGS, api, *objs, "-o", tmp]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"link failed (ASan build):\n{p.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
+def asan_runtime() -> str:
+    """The ASan runtime of the compiler that builds the library."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(_hipcc())), "..", "lib", "llvm", "bin",
+                         "clang")
+    for c in (clang, "/opt/rocm/llvm/bin/clang"):
+        if os.path.exists(c):
+            p = subprocess.run([c, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                               capture_output=True, text=True)
+            path = p.stdout.strip()
+            if p.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("the compiler's ASan runtime was not found")
+
+
 def build_all(verbose: bool = False) -> list:
     """The product library and the probe build."""
     return [build(LIB, verbose=verbose), build(PROBE_LIB, PROBE_FLAGS, verbose=verbose)]

@@ -25,6 +25,19 @@ def build(out: str = LIB, src: str = SRC, extra=()) -> str:
     return out
 
 
+def build_asan(out: str = os.path.join(HERE, "_asan", "libqsa_oracle_asan.so")) -> str:
+    """The oracle with host AddressSanitizer (gcc's runtime: load it with
+    asan_runtime() preloaded)."""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    return build(out, extra=("-fsanitize=address", "-fno-omit-frame-pointer", "-g"))
+
+
+def asan_runtime() -> str:
+    p = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True, text=True,
+                       check=True)
+    return os.path.realpath(p.stdout.strip())
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--out", default=LIB)
