@@ -661,10 +661,15 @@ static int ks_ranges(int64_t max_q, int64_t sub_tokens) {
   return (ks_groups(max_q, sub_tokens) + kRangeGroups - 1) / kRangeGroups;
 }
 
-int64_t ks_item_bound(const Geo& g, int64_t max_q, int64_t sub_tokens) {
+// Item slots of a sub-batch of n_tokens queries cut into nr query ranges per
+// sequence: the end of the last sequence's region under item_base.
+static int64_t ks_item_slots(const Geo& g, int nr, int64_t n_tokens) {
   const int64_t k1 = g.k + 1, nb1 = g.nbcap + 1;
-  return sub_tokens * k1 / ks_item_tokens(g) +
-         (int64_t)g.B * (ks_ranges(max_q, sub_tokens) * nb1 + 1);
+  return n_tokens * k1 / ks_item_tokens(g) + (int64_t)g.B * (nr * nb1 + 1);
+}
+
+int64_t ks_item_bound(const Geo& g, int64_t max_q, int64_t sub_tokens) {
+  return ks_item_slots(g, ks_ranges(max_q, sub_tokens), sub_tokens);
 }
 
 hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const void* k_cache,
@@ -688,7 +693,9 @@ hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const 
   for (int t_lo = 0; t_lo < g.T; t_lo += w.sub_tokens) {
     a.t_lo = t_lo;
     a.t_hi = std::min(g.T, t_lo + w.sub_tokens);
-    const int n_items = (int)ks_item_bound(g, w.max_q, a.t_hi - a.t_lo);
+    // (a.nr, as the plan kernels' item_base uses it: a short last sub-batch
+    // keeps the ranges of a full one)
+    const int n_items = (int)ks_item_slots(g, a.nr, a.t_hi - a.t_lo);
     a.n_items = n_items;
     if (a.qrot != nullptr)
       ks_rotate_q_kernel<<<(int)(((int64_t)(a.t_hi - a.t_lo) * g.Hq + 3) / 4), 256, 0, st>>>(

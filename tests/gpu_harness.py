@@ -115,6 +115,8 @@ def check_call(dc, seqf: SeqF32, result, sample: Optional[int] = None, rng_seed:
     worst = {"max_abs": 0.0, "mean_abs": 0.0, "max_rel": 0.0, "rows": 0, "exempt": 0}
     for b, (s, e) in enumerate(spans):
         n_q = e - s
+        if n_q == 0:
+            continue  # a sequence with no new tokens in this call: no output rows
         idx = np.arange(n_q)
         if sample is not None and n_q > sample:
             idx = np.sort(rng.choice(n_q, size=sample, replace=False))

@@ -27,7 +27,10 @@ def _full(case, sample=None, keep=None, layout=None, **kw):
     dc = runner.DeviceCase(case, layout=layout, **kw)
     res = run_calls(dc, keep=keep)
     seqf = SeqF32(case)
-    stats = [check_call(dc, seqf, res[i], sample=sample, rng_seed=i) for i in sorted(res)]
+    stats = []
+    for i in sorted(res):
+        say(f"  checking call {i}")
+        stats.append(check_call(dc, seqf, res[i], sample=sample, rng_seed=i))
     say("  stats", stats[-1])
     return dc, res, stats
 
@@ -337,3 +340,18 @@ def test_repeated_attend_reuses_workspace():
                            outs["n_blocks"], inp["gate"], again, outs["ws"])
             torch.cuda.synchronize()
             assert torch.equal(again, first), name
+
+
+def test_ragged_prefill_across_sub_batches():
+    """Several sequences' prefill chunks in one call, more new tokens than one
+    sub-batch of the key-stationary path holds: a sequence split across two
+    sub-batches, and a short chunk alone in the second sub-batch."""
+    import dataclasses
+    sp = dataclasses.replace(workloads.SPECS["chunked_prefill_32k_bf16"], n_seqs=3,
+                             prefill_len=4096)
+    case = workloads._draw(sp, 0)
+    case.calls = [[(0, 2048), (0, 2048), (0, 2048)],
+                  [(2048, 4096), (2048, 4096), (2048, 2060)],
+                  [(4096, 4096), (4096, 4096), (2060, 2100)]]
+    _full(case, sample=64)
+    _full(case, sample=64, layout="paged")
