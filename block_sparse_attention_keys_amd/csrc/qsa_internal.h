@@ -145,7 +145,8 @@ struct KsArgs {
   int32_t nr;            // query ranges per sequence (of the work-item order)
   int32_t n_items;       // work-item slots of this sub-batch
   uint32_t* list;        // [sub * k1] entries, grouped by block
-  int32_t* hist;         // [B][ng][nb1] entries per (group, block)
+  int32_t* hist;         // [B][ng][nb1] entries per (group, block); after the scan, per
+                         // (group, block) the entries of the block from earlier groups
   int32_t* boff;         // [B][nb1] first list position of each block
   int4* items;           // [ks_item_bound] work items {list start, block, count, sequence}
   uint16_t* po;          // [sub][k1][Hq][D] bf16 partial outputs, normalised

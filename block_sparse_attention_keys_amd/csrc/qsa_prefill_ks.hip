@@ -58,6 +58,10 @@ constexpr int kRows = 64;    // (query, head) rows per tile of ks_attn (4 waves 
 constexpr int kGroup = 64;   // queries per counting group of the plan
 constexpr int kRangeGroups = 16;  // groups per query range of the work-item order
 constexpr int kScanThreads = 1024;
+// Query ranges per sequence in one sub-batch (the scan keeps a register per
+// range and block).
+constexpr int kMaxRanges = kKsSubTokens / (kGroup * kRangeGroups);
+static_assert(kMaxRanges * kGroup * kRangeGroups == kKsSubTokens, "sub-batch cut into whole ranges");
 
 // Entries of a block's query list: the query's index in the call and its slot
 // (position in its selection, or k for the tail), packed as t << 12 | slot.
@@ -152,50 +156,57 @@ __device__ __forceinline__ int scan_excl(int v, int* total, int* sh) {
 // block, groups in order).  Work items are cut per (query range of
 // kRangeGroups groups, block), ranges outermost: items dispatched together
 // then read the queries of one range, which stay in the L2 of their XCD.
-// Unused item slots of the sequence's region are written empty.
+// Unused item slots of the sequence's region are written empty.  The
+// histogram is read once, 32 or 64 loads per thread in flight at a time, and its
+// per-range sums stay in registers for both scans.
 template <int PER>  // consecutive blocks per thread (PER * kScanThreads >= nb1)
 __global__ __launch_bounds__(kScanThreads) void ks_scan_kernel(Geo g, KsArgs a) {
   __shared__ int sh[kScanThreads / 64];
   const int b = blockIdx.x, tid = threadIdx.x;
   const SeqRange sr = seq_range(g, a, b);
   const int NB1 = a.nb1, ng = a.ng;
-  const int32_t* rows = a.hist + (int64_t)b * ng * NB1;
+  int32_t* rows = a.hist + (int64_t)b * ng * NB1;
   const int j0 = tid * PER;
-  // per (range, block) counts, one range at a time
-  auto range_counts = [&](int r, int (&c)[PER]) {
+  // c[r][i]: entries of block j0 + i from the groups of range r.  Each row
+  // of the histogram is replaced by the entries of the block from the groups
+  // before it (the scatter's offset inside the block's list).
+  int c[kMaxRanges][PER], run[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) c[i] = 0;
-    if (j0 >= NB1) return;
-    const int g1 = min(ng, (r + 1) * kRangeGroups);
-    constexpr int GB = PER >= 8 ? 8 : kRangeGroups;  // group rows loaded together
-#pragma unroll 1
-    for (int x0 = 0; x0 < kRangeGroups; x0 += GB) {
+  for (int i = 0; i < PER; ++i) {
+    run[i] = 0;
+#pragma unroll
+    for (int r = 0; r < kMaxRanges; ++r) c[r][i] = 0;
+  }
+  if (j0 < NB1) {
+    constexpr int GB = (PER == 1 ? 64 : 32) / PER;  // group rows per batch
+#pragma unroll
+    for (int g0 = 0; g0 < kMaxRanges * kRangeGroups; g0 += GB) {
+      if (g0 >= ng) break;
       int v[GB][PER];
 #pragma unroll
       for (int x = 0; x < GB; ++x)
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-          const int gi = r * kRangeGroups + x0 + x;
-          v[x][i] = (gi < g1 && j0 + i < NB1) ? rows[(int64_t)gi * NB1 + j0 + i] : 0;
-        }
+        for (int i = 0; i < PER; ++i)
+          v[x][i] = (g0 + x < ng && j0 + i < NB1) ? rows[(int64_t)(g0 + x) * NB1 + j0 + i] : 0;
 #pragma unroll
       for (int x = 0; x < GB; ++x)
 #pragma unroll
-        for (int i = 0; i < PER; ++i) c[i] += v[x][i];
+        for (int i = 0; i < PER; ++i) {
+          if (g0 + x < ng && j0 + i < NB1) rows[(int64_t)(g0 + x) * NB1 + j0 + i] = run[i];
+          run[i] += v[x][i];
+          c[(g0 + x) / kRangeGroups][i] += v[x][i];
+        }
     }
-  };
+  }
   const int n_ranges = (ng + kRangeGroups - 1) / kRangeGroups;
   int tot[PER], ents = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) tot[i] = 0;
-  for (int r = 0; r < n_ranges; ++r) {
-    int c[PER];
-    range_counts(r, c);
+  for (int i = 0; i < PER; ++i) {
+    tot[i] = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) tot[i] += c[i];
+    for (int r = 0; r < kMaxRanges; ++r) tot[i] += c[r][i];
+    ents += tot[i];
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) ents += tot[i];
   int total_ents;
   const int ent_before = scan_excl(ents, &total_ents, sh);
   const int list0 = (sr.t0 - a.t_lo) * a.k1;  // the sequence's list region
@@ -213,18 +224,19 @@ __global__ __launch_bounds__(kScanThreads) void ks_scan_kernel(Geo g, KsArgs a) 
   const int base = item_base(a, b, sr.t0 - a.t_lo);
   const int base_next = item_base(a, b + 1, sr.t1 - a.t_lo);
   int it0 = base;
-  for (int r = 0; r < n_ranges; ++r) {
-    int c[PER], items = 0;
-    range_counts(r, c);
 #pragma unroll
-    for (int i = 0; i < PER; ++i) items += (c[i] + a.item_tokens - 1) / a.item_tokens;
+  for (int r = 0; r < kMaxRanges; ++r) {
+    if (r >= n_ranges) break;  // uniform: every thread reaches the same scans
+    int items = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) items += (c[r][i] + a.item_tokens - 1) / a.item_tokens;
     int total_items;
     int it = it0 + scan_excl(items, &total_items, sh);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      for (int x = 0; x < c[i]; x += a.item_tokens, ++it)
-        a.items[it] = make_int4(pos[i] + x, j0 + i, min(a.item_tokens, c[i] - x), b);
-      pos[i] += c[i];
+      for (int x = 0; x < c[r][i]; x += a.item_tokens, ++it)
+        a.items[it] = make_int4(pos[i] + x, j0 + i, min(a.item_tokens, c[r][i] - x), b);
+      pos[i] += c[r][i];
     }
     it0 += total_items;
   }
@@ -233,31 +245,20 @@ __global__ __launch_bounds__(kScanThreads) void ks_scan_kernel(Geo g, KsArgs a) 
 
 // Plan, step 3: grid (query group, sequence).  Each entry goes to its
 // block's list at the block's first position, plus the entries of the
-// block from earlier groups, plus its rank among this group's entries of
-// the block.
+// block from earlier groups (the scan left them in the group's histogram
+// row), plus its rank among this group's entries of the block.
 __global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
                                                         const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ nblk) {
   extern __shared__ int32_t pos_lds[];
-  constexpr int GB = 16;
   const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const SeqRange sr = seq_range(g, a, b);
   const int ta = min(sr.t0 + gi * kGroup, sr.t1), tb = min(sr.t1, ta + kGroup);
   if (ta >= tb) return;
   const int past = g.past_len[b], cu0 = g.cu_q[b], K1 = a.k1, NB1 = a.nb1;
-  const int32_t* rows = a.hist + (int64_t)b * a.ng * NB1;
+  const int32_t* before = a.hist + ((int64_t)b * a.ng + gi) * NB1;
   const int32_t* boff = a.boff + (int64_t)b * NB1;
-  for (int j = tid; j < NB1; j += 256) {
-    int acc = boff[j];
-    for (int g0 = 0; g0 < gi; g0 += GB) {
-      int v[GB];
-#pragma unroll
-      for (int x = 0; x < GB; ++x) v[x] = g0 + x < gi ? rows[(int64_t)(g0 + x) * NB1 + j] : 0;
-#pragma unroll
-      for (int x = 0; x < GB; ++x) acc += v[x];
-    }
-    pos_lds[j] = acc;
-  }
+  for (int j = tid; j < NB1; j += 256) pos_lds[j] = boff[j] + before[j];
   __syncthreads();
   for (int e = tid; e < (tb - ta) * K1; e += 256) {
     const int t = ta + e / K1, slot = e - (e / K1) * K1;
@@ -582,13 +583,16 @@ __global__ __launch_bounds__(256) void ks_merge_kernel(Geo g, KsArgs a,
     float cm = M;
 #pragma unroll
     for (int u = 0; u < kU; ++u) cm = fmaxf(cm, lv[u]);
-    const float sc = (M == -INFINITY) ? 0.0f : exp2f(M - cm);
+    // (the hardware exp2: exp2(-inf) = 0 for the invalid slots; a round with
+    // none valid so far leaves everything at zero)
+    const float sc = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(M - cm);
     den *= sc;
 #pragma unroll
     for (int x = 0; x < 8; ++x) acc[x] *= sc;
+    const float cmv = cm == -INFINITY ? 0.0f : cm;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const float w = lv[u] != -INFINITY ? exp2f(lv[u] - cm) : 0.0f;
+      const float w = __builtin_amdgcn_exp2f(lv[u] - cmv);
       const uint32_t wv[4] = {ov[u].x, ov[u].y, ov[u].z, ov[u].w};
       den += w;
 #pragma unroll
@@ -682,6 +686,7 @@ hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const 
   a.item_tokens = ks_item_tokens(g);
   a.ng = ks_groups(w.max_q, w.sub_tokens);
   a.nr = ks_ranges(w.max_q, w.sub_tokens);
+  if (w.sub_tokens > kKsSubTokens || a.nr > kMaxRanges) return hipErrorInvalidValue;
   a.list = w.list;
   a.items = w.items;
   a.hist = w.hist;

@@ -355,3 +355,17 @@ def test_ragged_prefill_across_sub_batches():
                   [(4096, 4096), (4096, 4096), (2060, 2100)]]
     _full(case, sample=64)
     _full(case, sample=64, layout="paged")
+
+
+@pytest.mark.parametrize("n_tok", [40000, 80000, 140000])
+def test_prefill_key_stationary_many_candidate_blocks(n_tok):
+    """Block size 32 over 40K, 80K and 140K tokens: 1251, 2501 and 4376
+    candidate blocks, so the plan's scan takes 2, 4 and 8 blocks per thread.
+    One call prefills all but the last 1024 tokens (tens of sub-batches), the
+    next the rest."""
+    import dataclasses
+    sp = dataclasses.replace(workloads.SPECS["chunked_prefill_32k_bf16"], block_size=32,
+                             budget=2048, prefill_len=n_tok)
+    case = workloads._draw(sp, 0)
+    case.calls = [[(0, n_tok - 1024)], [(n_tok - 1024, n_tok)]]
+    _full(case, sample=24)
