@@ -446,13 +446,18 @@ def bench_prefill(args, name):
     calls = [dc.call_inputs(i) for i in range(len(case.calls))]
     outs = [dc.alloc_outputs(x) for x in calls]
     r, k = sp.block_size, sp.k_blocks
-    flops = []
+    flops, algo = [], []
+    kv_row = sp.n_kv_heads * sp.head_dim * (1 if sp.kv_fp8 else 2)  # bytes per K (or V) row
     for x in calls:
         s0, e0 = x["spans"][0]
         n = np.arange(s0, e0) + 1
         nb = n // r
         nsel = r * np.minimum(k, nb) + (n - r * nb)
         flops.append(float((nsel * sp.n_q_heads * 4 * sp.head_dim).sum()))
+        # algorithmic bytes of one qsa_attend launch: q, gate and out; the
+        # selections and counts; each K/V row of the prefix once
+        T = e0 - s0
+        algo.append(3 * T * sp.n_q_heads * sp.head_dim * 2 + T * (k + 1) * 4 + e0 * kv_row * 2)
     total_flops = sum(flops)
     stream = torch.cuda.current_stream()
 
@@ -500,7 +505,9 @@ def bench_prefill(args, name):
                      "achieved": round(attn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                      "avg_launch_us": round(float(np.mean(attn_ms)) * 1e3, 1),
-                     "flops_per_launch": round(total_flops / len(calls)), "traffic": None},
+                     "flops_per_launch": round(total_flops / len(calls)),
+                     "bytes_per_launch": round(sum(algo) / len(calls)),
+                     "traffic": counter_traffic(f"attn_{name}_hbm_counters.txt")},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(case, sp, args.cpu_seconds)
