@@ -306,8 +306,10 @@ __global__ __launch_bounds__(256) void ks_rotate_q_kernel(Geo g, KsArgs a,
 //     of the 288-byte V rows) x P^T (B: p straight from the softmax
 //     registers; key order inside a 32-key step follows the accumulator
 //     layout, and V follows it): with V's dims placed as below, a lane holds
-//     row c16's dims 32 m + 8 grp .. +7 in tiles 2 m and 2 m + 1, stored as
-//     16 bytes.
+//     row c16's dims 32 m + 8 grp .. +7 in tiles 2 m and 2 m + 1;
+//   the wave's 16 rows of o / l (bf16) are exchanged through LDS and stored 4
+//     whole rows per instruction, whole 128-byte lines (half-line stores of
+//     the same bytes cost about 27 % more HBM writes and 6 % of the prefill).
 // KV8: the caches hold E4M3 codes (one byte per element), turned into bf16
 // (exactly) as they go to LDS; the scales and the rotation are in the
 // softmax scale, the rotated query (ks_rotate_q_kernel) and the merge.
@@ -323,6 +325,7 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
   __shared__ __attribute__((aligned(16))) unsigned char Kl[RB * KS];
   __shared__ __attribute__((aligned(16))) unsigned char Vl[RB * VS];
   __shared__ int32_t s_t[kKsItemMax], s_slot[kKsItemMax], s_p[kKsItemMax];
+  __shared__ __attribute__((aligned(16))) uint4 Os[4][16 * 16];  // a wave's 16 output rows
   // Workgroups go round-robin over the 8 XCDs (blockIdx % 8).  When Hkv
   // divides 8, XCD x serves KV head x / (8 / Hkv) and items of its residue,
   // in item order: the items an XCD runs together read one query range.
@@ -500,24 +503,39 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
     }
     // Partial state of row c16: o / l as bf16 (dims 16 nd + 4 grp .. +3), and
     // the base-2 log-sum-exp.
-    if (rw.t >= 0) {
-      const int64_t row = ((int64_t)(rw.t - a.t_lo) * a.k1 + rw.slot) * g.Hq + h0 + hh;
-      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-      uint16_t* dst = a.po + row * D + 8 * grp;
+    // The wave's 16 rows go through LDS (16-byte chunks XOR-swizzled by
+    // row) so that each store instruction writes 4 whole rows: 1 KB
+    // contiguous when they are one query's heads.
+    const int row = rw.t >= 0 ? ((rw.t - a.t_lo) * a.k1 + rw.slot) * g.Hq + h0 + hh : -1;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint4* os = Os[wid];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint32_t w[4];
+    for (int m = 0; m < 4; ++m) {
+      uint32_t w[4];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const f32x4_t& o = O[2 * m + x];
-          w[2 * x] = pack_bf16(o[0] * inv, o[1] * inv);
-          w[2 * x + 1] = pack_bf16(o[2] * inv, o[3] * inv);
-        }
-        __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]},
-                                    reinterpret_cast<u32x4_t*>(dst + 32 * m));
+      for (int x = 0; x < 2; ++x) {
+        const f32x4_t& o = O[2 * m + x];
+        w[2 * x] = pack_bf16(o[0] * inv, o[1] * inv);
+        w[2 * x + 1] = pack_bf16(o[2] * inv, o[3] * inv);
       }
-      if (grp == 0) a.pl[row] = l > 0.0f ? mb + log2f(l) : -INFINITY;
+      os[c16 * 16 + ((4 * m + grp) ^ c16)] = make_uint4(w[0], w[1], w[2], w[3]);
     }
+    if (grp == 0 && row >= 0) a.pl[row] = l > 0.0f ? mb + log2f(l) : -INFINITY;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = 4 * i + (lane >> 4), ch = lane & 15;
+      const int orow = __shfl(row, rr, 64);
+      const uint4 v = os[rr * 16 + (ch ^ rr)];
+      if (orow >= 0)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v),
+                                    reinterpret_cast<u32x4_t*>(a.po + (int64_t)orow * D + 8 * ch));
+    }
+    // (the next tile's writes to Os wait for these reads: in-order LDS
+    // traffic of one wave)
+    __builtin_amdgcn_wave_barrier();
   };
   // Two row buffers: the loads of tile c + 2 are requested once tile c is
   // done with its buffer, and arrive while tile c + 1 computes.
