@@ -301,7 +301,8 @@ __global__ __launch_bounds__(256) void ks_rotate_q_kernel(Geo g, KsArgs a,
 //     (B: the row's query, 16 bytes from memory, the next tile's requested
 //     during this one): a lane holds row c16's scores of keys 16 n + 4 grp + r;
 //   the row's softmax over the block's keys it may see (causal mask), in
-//     base 2: in-lane over 4 KT keys, then two row swaps; p rounded to bf16;
+//     base 2: in-lane over 4 KT keys, then two row swaps; p / l rounded to
+//     bf16 (l the fp32 sum of the row's p), so the product below is normalised;
 //   O^T[dim][row] = V^T (A: a dim's 8 keys through two transposing LDS reads
 //     of the 288-byte V rows) x P^T (B: p straight from the softmax
 //     registers; key order inside a 32-key step follows the accumulator
@@ -469,19 +470,24 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
     mx = max_xor32(max_xor16(mx));
     // a row with no visible key: every p is 0 (exp2(-inf) = 0)
     const float mb = mx == -INFINITY ? 0.0f : mx * sc;
-    uint32_t pw[KT][2];
+    // p / l rounded to bf16 for the matrix cores: the block's partial output
+    // comes out normalised
+    float pe[KT][4];
     float lsum = 0.0f;
 #pragma unroll
     for (int n = 0; n < KT; ++n)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // the denominator sums the bf16-rounded p
-        const uint32_t pp = pack_bf16(__builtin_amdgcn_exp2f(fmaf(S[n][2 * h], sc, -mb)),
-                                      __builtin_amdgcn_exp2f(fmaf(S[n][2 * h + 1], sc, -mb)));
-        lsum += bf_lo(pp) + bf_hi(pp);
-        pw[n][h] = pp;
+      for (int r = 0; r < 4; ++r) {
+        pe[n][r] = __builtin_amdgcn_exp2f(fmaf(S[n][r], sc, -mb));
+        lsum += pe[n][r];
       }
     const float l = sum_xor32(sum_xor16(lsum));
+    const float inv = l > 0.0f ? __builtin_amdgcn_rcpf(l) : 0.0f;
+    uint32_t pw[KT][2];
+#pragma unroll
+    for (int n = 0; n < KT; ++n)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) pw[n][h] = pack_bf16(pe[n][2 * h] * inv, pe[n][2 * h + 1] * inv);
     // O^T = V^T P^T
     f32x4_t O[8];
 #pragma unroll
@@ -501,13 +507,12 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
                                                         ks == 0 ? zero4 : O[nd], 0, 0, 0);
       }
     }
-    // Partial state of row c16: o / l as bf16 (dims 16 nd + 4 grp .. +3), and
-    // the base-2 log-sum-exp.
+    // Partial state of row c16: o (already divided by l) as bf16 (dims
+    // 16 nd + 4 grp .. +3), and the base-2 log-sum-exp.
     // The wave's 16 rows go through LDS (16-byte chunks XOR-swizzled by
     // row) so that each store instruction writes 4 whole rows: 1 KB
     // contiguous when they are one query's heads.
     const int row = rw.t >= 0 ? ((rw.t - a.t_lo) * a.k1 + rw.slot) * g.Hq + h0 + hh : -1;
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     uint4* os = Os[wid];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -515,12 +520,12 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         const f32x4_t& o = O[2 * m + x];
-        w[2 * x] = pack_bf16(o[0] * inv, o[1] * inv);
-        w[2 * x + 1] = pack_bf16(o[2] * inv, o[3] * inv);
+        w[2 * x] = pack_bf16(o[0], o[1]);
+        w[2 * x + 1] = pack_bf16(o[2], o[3]);
       }
       os[c16 * 16 + ((4 * m + grp) ^ c16)] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    if (grp == 0 && row >= 0) a.pl[row] = l > 0.0f ? mb + log2f(l) : -INFINITY;
+    if (grp == 0 && row >= 0) a.pl[row] = l > 0.0f ? mb + __builtin_amdgcn_logf(l) : -INFINITY;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
