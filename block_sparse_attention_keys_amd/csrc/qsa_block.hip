@@ -254,11 +254,41 @@ __device__ QueryPosB token_pos(const Geo& g, int t) {
   return {p, p >= 0 && p < g.cap};
 }
 
-// Grid (token, group of 4 rows); one wave per row of the stacked input
-// projection: q heads, gate heads, k heads, v heads, indexer-query heads,
-// the indexer key.  Lane l holds values l and l + 64 of a row.
+// Grid (token, group of 4 RPW rows); each wave takes RPW consecutive rows of
+// the stacked input projection (q heads, gate heads, k heads, v heads,
+// indexer-query heads, the indexer key), requests the partial sums of all of
+// them before it uses the first, then finishes them one by one.  Lane l
+// holds values l and l + 64 of a row.
+struct PrepRow {
+  int kind, head, base, len;  // kind: 0 q, 1 gate, 2 k, 3 v, 4 indexer q, 5 indexer k
+};
+__device__ __forceinline__ PrepRow prep_row(const Geo& g, int rw) {
+  const int D = g.D, Hq = g.Hq, Hkv = g.Hkv, HI = g.HI, dI = g.dI;
+  if (rw < Hq) return {0, rw, rw * D, D};
+  if (rw < 2 * Hq) return {1, rw - Hq, rw * D, D};
+  if (rw < 2 * Hq + Hkv) return {2, rw - 2 * Hq, rw * D, D};
+  if (rw < 2 * Hq + 2 * Hkv) return {3, rw - 2 * Hq - Hkv, rw * D, D};
+  if (rw < 2 * Hq + 2 * Hkv + HI) {
+    const int head = rw - 2 * Hq - 2 * Hkv;
+    return {4, head, (2 * Hq + 2 * Hkv) * D + head * dI, dI};
+  }
+  return {5, 0, (2 * Hq + 2 * Hkv) * D + HI * dI, dI};
+}
+
+// Rotate-half at value x of a row with the token's factors c[i] = cos(pos f_i),
+// s[i] = sin(pos f_i) (computed in fp64, rounded to fp32).
+__device__ __forceinline__ float rope_tab(const float* row, int x, int R, const float* c,
+                                          const float* s) {
+  if (x >= R) return row[x];
+  const int h = R >> 1, i = x < h ? x : x - h;
+  if (x < h) return row[x] * c[i] - row[x + h] * s[i];
+  return row[x] * c[i] + row[i] * s[i];
+}
+
+template <int RPW, bool ONE_SPLIT>  // ONE_SPLIT: a.S == 1 (loads need no split sums)
 __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a) {
   __shared__ float rowbuf[4][128];
+  __shared__ float cos_tab[2][64], sin_tab[2][64];  // [q/k, indexer q][frequency]
   const int t = blockIdx.x, wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (g.r > 0 && blockIdx.y == 0 && threadIdx.x < g.HI) a.w[(int64_t)t * g.HI + threadIdx.x] = 1.0f;
   const QueryPosB qp = token_pos(g, t);
@@ -268,54 +298,79 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
   const int64_t MN = (int64_t)g.T * a.n_in;
   const float* P = a.part + (int64_t)t * a.n_in;
   float* row = rowbuf[wid];
-  const int rw = blockIdx.y * 4 + wid;
-  if (rw < n_rows) {
-    int kind, head, base, len;  // kind: 0 q, 1 gate, 2 k, 3 v, 4 indexer q, 5 indexer k
-    if (rw < Hq) { kind = 0; head = rw; base = head * D; len = D; }
-    else if (rw < 2 * Hq) { kind = 1; head = rw - Hq; base = (Hq + head) * D; len = D; }
-    else if (rw < 2 * Hq + Hkv) { kind = 2; head = rw - 2 * Hq; base = (2 * Hq + head) * D; len = D; }
-    else if (rw < 2 * Hq + 2 * Hkv) {
-      kind = 3; head = rw - 2 * Hq - Hkv; base = (2 * Hq + Hkv + head) * D; len = D;
-    } else if (rw < 2 * Hq + 2 * Hkv + HI) {
-      kind = 4; head = rw - 2 * Hq - 2 * Hkv; base = (2 * Hq + 2 * Hkv) * D + head * dI; len = dI;
-    } else {
-      kind = 5; head = 0; base = (2 * Hq + 2 * Hkv) * D + HI * dI; len = dI;
-    }
-    float v[2];
+  const int rw0 = (blockIdx.y * 4 + wid) * RPW;
+  // requested first (loads complete in order): this thread's rotary
+  // frequency and the two norm weights' values of lanes l and l + 64
+  const int tab_which = threadIdx.x >> 6, tab_i = threadIdx.x & 63;
+  const int tab_R = tab_which ? g.idx_rope_dim : a.rotary_dim;
+  const bool tab_on = threadIdx.x < 128 && tab_i < (tab_R >> 1);
+  const double tab_f = tab_on ? (tab_which ? a.idx_freq[tab_i] : a.freq[tab_i]) : 0.0;
+  float qn[2], kn[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int x = min(lane + 64 * e, D - 1);
+    qn[e] = to_f32(a.q_norm[x]);
+    kn[e] = to_f32(a.k_norm[x]);
+  }
+  float v[RPW][2];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    const PrepRow pr = prep_row(g, rw0 + i);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int x = lane + 64 * e;
-      v[e] = x < len ? sum_parts(P, a.S, MN, base + x) : 0.0f;
+      const bool ok = rw0 + i < n_rows && x < pr.len;
+      if constexpr (ONE_SPLIT) {
+        // unconditional loads (at value 0 of the token for absent ones), so
+        // all of them are in flight together
+        const float val = P[ok ? pr.base + x : 0];
+        v[i][e] = ok ? val : 0.0f;
+      } else {
+        v[i][e] = ok ? sum_parts(P, a.S, MN, pr.base + x) : 0.0f;
+      }
     }
+  }
+  // the token's rotary factors, once per workgroup (every rotated row of the
+  // token uses the same 2 x 32 angles), computed while the loads are in flight
+  if (tab_on) {
+    const double ang = (double)pos * tab_f;
+    cos_tab[tab_which][tab_i] = (float)cos(ang);
+    sin_tab[tab_which][tab_i] = (float)sin(ang);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) {
+    if (rw0 + i >= n_rows) break;
+    const PrepRow pr = prep_row(g, rw0 + i);
+    const int kind = pr.kind, head = pr.head, len = pr.len;
+    float* vr = v[i];
     if (kind == 0 || kind == 2) {
       // RMSNorm over the head, weight (1 + w).
-      const float ss = wave_sum(v[0] * v[0] + v[1] * v[1]);
+      const float ss = wave_sum(vr[0] * vr[0] + vr[1] * vr[1]);
       const float inv = 1.0f / sqrtf(ss / (float)len + a.eps);
-      const uint16_t* w = kind == 0 ? a.q_norm : a.k_norm;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int x = lane + 64 * e;
-        if (x < len) v[e] = (v[e] * inv) * (1.0f + to_f32(w[x]));
+        if (x < len) vr[e] = (vr[e] * inv) * (1.0f + (kind == 0 ? qn[e] : kn[e]));
       }
     }
     if (kind == 0 || kind == 2 || kind == 4) {
       const int R = kind == 4 ? g.idx_rope_dim : a.rotary_dim;
       if (R > 0) {
+        wave_sync();  // the previous row's reads of the buffer are done
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-          if (lane + 64 * e < len) row[lane + 64 * e] = v[e];
+          if (lane + 64 * e < len) row[lane + 64 * e] = vr[e];
         wave_sync();
         float rv[2];
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int x = lane + 64 * e;
-          // (one call per table: no pointer chosen at run time)
-          rv[e] = x >= len ? 0.0f
-                  : kind == 4 ? rope_at(row, x, R, a.idx_freq, pos)
-                              : rope_at(row, x, R, a.freq, pos);
+          const int which = kind == 4 ? 1 : 0;
+          rv[e] = x >= len ? 0.0f : rope_tab(row, x, R, cos_tab[which], sin_tab[which]);
         }
-        v[0] = rv[0];
-        v[1] = rv[1];
+        vr[0] = rv[0];
+        vr[1] = rv[1];
       }
     }
     uint16_t* dst;
@@ -330,7 +385,7 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int x = lane + 64 * e;
-      if (x < len) dst[x] = bf16_rne(v[e]);
+      if (x < len) dst[x] = bf16_rne(vr[e]);
     }
   }
 }
@@ -378,7 +433,11 @@ hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, h
 
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st) {
   const int n_rows = 2 * g.Hq + 2 * g.Hkv + (g.r > 0 ? g.HI + 1 : 0);
-  block_prep_kernel<<<dim3(g.T, (n_rows + 3) / 4), 256, 0, st>>>(g, a);
+  // prefill-sized calls: 4 rows per wave (loads of all four in flight);
+  // decode-sized ones keep one row per wave and more workgroups
+  if (g.T >= 512 && a.S == 1)
+    block_prep_kernel<4, true><<<dim3(g.T, (n_rows + 15) / 16), 256, 0, st>>>(g, a);
+  else block_prep_kernel<1, false><<<dim3(g.T, (n_rows + 3) / 4), 256, 0, st>>>(g, a);
   return hipGetLastError();
 }
 
