@@ -301,9 +301,14 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
   const int rw0 = (blockIdx.y * 4 + wid) * RPW;
   // requested first (loads complete in order): this thread's rotary
   // frequency and the two norm weights' values of lanes l and l + 64
+  // (the table only where the workgroup holds a q, k or indexer-q row)
+  const int wg_lo = blockIdx.y * 4 * RPW, wg_hi = min(n_rows, wg_lo + 4 * RPW);
+  const auto overlaps = [&](int lo, int hi) { return wg_lo < hi && lo < wg_hi; };
+  const bool need_tab = overlaps(0, Hq) || overlaps(2 * Hq, 2 * Hq + Hkv) ||
+                        (g.r > 0 && overlaps(2 * Hq + 2 * Hkv, 2 * Hq + 2 * Hkv + HI));
   const int tab_which = threadIdx.x >> 6, tab_i = threadIdx.x & 63;
   const int tab_R = tab_which ? g.idx_rope_dim : a.rotary_dim;
-  const bool tab_on = threadIdx.x < 128 && tab_i < (tab_R >> 1);
+  const bool tab_on = need_tab && threadIdx.x < 128 && tab_i < (tab_R >> 1);
   const double tab_f = tab_on ? (tab_which ? a.idx_freq[tab_i] : a.freq[tab_i]) : 0.0;
   float qn[2], kn[2];
 #pragma unroll
@@ -332,12 +337,15 @@ __global__ __launch_bounds__(256) void block_prep_kernel(Geo g, BlockPrepArgs a)
   }
   // the token's rotary factors, once per workgroup (every rotated row of the
   // token uses the same 2 x 32 angles), computed while the loads are in flight
-  if (tab_on) {
-    const double ang = (double)pos * tab_f;
-    cos_tab[tab_which][tab_i] = (float)cos(ang);
-    sin_tab[tab_which][tab_i] = (float)sin(ang);
+  if (need_tab) {  // uniform over the workgroup
+    if (tab_on) {
+      double sn, cs;
+      sincos((double)pos * tab_f, &sn, &cs);
+      cos_tab[tab_which][tab_i] = (float)cs;
+      sin_tab[tab_which][tab_i] = (float)sn;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 #pragma unroll
   for (int i = 0; i < RPW; ++i) {
     if (rw0 + i >= n_rows) break;
