@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libqsa.so")
 # debug build for tests: counts the K/V rows the attention kernels load
 PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
 PROBE_FLAGS = ["-DQSA_COUNT_KEYS"]
-SOURCES = ["qsa_api.hip", "qsa_kernels.hip", "qsa_block.hip", "qsa_prefill_ks.hip"]
+SOURCES = ["qsa_api.hip", "qsa_kernels.hip", "qsa_block.hip", "qsa_prefill_ks.hip", "qsa_blas.hip"]
 ARCH = "gfx950"
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -54,7 +54,7 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(comp, SOURCES))
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-ldl", "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
@@ -86,7 +86,8 @@ def build_asan() -> str:
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed on the ASan build:\n{p.stderr}")
     tmp = ASAN_LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *ASAN_FLAGS, api, *objs, "-o", tmp]
+    cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *ASAN_FLAGS, api, *objs, "-ldl",
+           "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed (ASan build):\n{p.stderr}")

@@ -421,6 +421,11 @@ hipError_t launch_proj_gemm(const void* A, const void* B, float* part, void* out
   const int ks = gemm_k_split(K, S);
   uint16_t* out = S == 1 ? static_cast<uint16_t*>(out_bf16) : nullptr;
   if (gemm_tiled(M, N) && S == 1) {
+    // a plain GEMM: hipBLASLt's tuned kernels where they run, else our own
+    const hipError_t e = lt_gemm(A, B, out != nullptr ? static_cast<void*>(out)
+                                                       : static_cast<void*>(part),
+                                 out == nullptr, M, N, K, st);
+    if (e != hipErrorNotSupported) return e;
     dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile);
     proj_gemm_tiled_kernel<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(A),
                                                  static_cast<const uint16_t*>(B), part, out, M, N,

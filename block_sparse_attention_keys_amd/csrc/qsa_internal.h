@@ -116,6 +116,10 @@ int gemm_k_split(int K, int S);
 hipError_t launch_proj_gemm(const void* A, const void* B, float* part, void* out_bf16, int M,
                             int N, int K, int S, hipStream_t st);
 hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, hipStream_t st);
+// D[M][N] = A[M][K] · B[N][K]ᵀ on hipBLASLt (qsa_blas.hip); hipErrorNotSupported
+// when it cannot run the product (the caller then runs its own kernel).
+hipError_t lt_gemm(const void* A, const void* B, void* D, bool d_f32, int M, int N, int K,
+                   hipStream_t st);
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st);
 
 #ifdef QSA_COUNT_KEYS
