@@ -124,84 +124,88 @@ __device__ __forceinline__ void store_rows_kv8(const Geo& g, const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// append + pool: one workgroup per new token.
+// append + pool: grid (new token, role).  Role 0 (dispatched first) pools the
+// block the token completes, if any; role 1 appends the token's rows.
 template <typename E>
 __global__ __launch_bounds__(256) void append_pool_kernel(
     Geo g, const E* __restrict__ k_new, const E* __restrict__ v_new,
     const E* __restrict__ kI_new, E* __restrict__ k_cache, E* __restrict__ v_cache,
     E* __restrict__ kI_cache, float* __restrict__ pooled, RopeTab rt) {
   const int t = blockIdx.x, tid = threadIdx.x;
+  const bool pool_role = blockIdx.y == 0;
+  if (pool_role && (pooled == nullptr || g.r == 0)) return;
   const QueryPos qp = query_pos(g, t);
   if (!qp.ok) return;
   constexpr int EPV = 16 / sizeof(E);  // elements per 16-byte copy
-  if (k_new != nullptr && g.kv8) {
-    if constexpr (sizeof(E) == 2) {
-      if (tid < 64)
-        store_rows_kv8(g, reinterpret_cast<const uint16_t*>(k_new) + (int64_t)t * g.Hkv * 128,
-                       reinterpret_cast<const uint16_t*>(v_new) + (int64_t)t * g.Hkv * 128,
-                       reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
-                       [&](int kvh) { return kv_row(g, qp.b, kvh, qp.p); });
+  if (!pool_role) {
+    if (k_new != nullptr && g.kv8) {
+      if constexpr (sizeof(E) == 2) {
+        if (tid < 64)
+          store_rows_kv8(g, reinterpret_cast<const uint16_t*>(k_new) + (int64_t)t * g.Hkv * 128,
+                         reinterpret_cast<const uint16_t*>(v_new) + (int64_t)t * g.Hkv * 128,
+                         reinterpret_cast<uint8_t*>(k_cache), reinterpret_cast<uint8_t*>(v_cache),
+                         [&](int kvh) { return kv_row(g, qp.b, kvh, qp.p); });
+      }
+    } else if (k_new != nullptr) {
+      const int units = g.D / EPV;
+      const int per = g.Hkv * units;
+      for (int u = tid; u < 2 * per; u += blockDim.x) {
+        const int which = u / per, rem = u - which * per;
+        const int kvh = rem / units, c = rem - kvh * units;
+        const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
+        if (dst < 0) continue;
+        const E* src = (which ? v_new : k_new) + ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV;
+        E* d = (which ? v_cache : k_cache) + dst + c * EPV;
+        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(src);
+      }
     }
-  } else if (k_new != nullptr) {
-    const int units = g.D / EPV;
-    const int per = g.Hkv * units;
-    for (int u = tid; u < 2 * per; u += blockDim.x) {
-      const int which = u / per, rem = u - which * per;
-      const int kvh = rem / units, c = rem - kvh * units;
-      const int64_t dst = kv_row(g, qp.b, kvh, qp.p);
-      if (dst < 0) continue;
-      const E* src = (which ? v_new : k_new) + ((int64_t)t * g.Hkv + kvh) * g.D + c * EPV;
-      E* d = (which ? v_cache : k_cache) + dst + c * EPV;
-      *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(src);
+    if (kI_new == nullptr) return;
+    const int64_t dst = idx_row(g, qp.b, qp.p);
+    if (dst >= 0) {
+      for (int u = tid; u < g.dI / EPV; u += blockDim.x)
+        *reinterpret_cast<uint4*>(kI_cache + dst + u * EPV) =
+            *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * g.dI + u * EPV);
     }
-  }
-  if (kI_new == nullptr) return;
-  const int64_t dst = idx_row(g, qp.b, qp.p);
-  if (dst >= 0) {
-    for (int u = tid; u < g.dI / EPV; u += blockDim.x)
-      *reinterpret_cast<uint4*>(kI_cache + dst + u * EPV) =
-          *reinterpret_cast<const uint4*>(kI_new + (int64_t)t * g.dI + u * EPV);
+    return;
   }
   // The token that ends block j pools it.  Rows appended by this same call are
   // read from kI_new (another workgroup may not have stored them yet); older
-  // rows come from the cache.  The rows are staged in LDS by all threads in
-  // parallel (32 at a time: 16 KB, which leaves room for 8 workgroups per CU);
-  // then one thread per column adds them in token order, so the sum is the
-  // sequential fp32 sum.
-  if (pooled == nullptr || g.r == 0 || ((qp.p + 1) & (g.r - 1)) != 0) return;
-  constexpr int kStageRows = 32;
-  __shared__ float stage[kStageRows * 128];
+  // rows come from the cache.  One thread per column adds the rows in token
+  // order (the sequential fp32 sum); its loads go out kPoolBatch rows at a
+  // time, all requested before the first add when the batch lies in this
+  // call's rows (a block of a prefill chunk, except where it straddles the
+  // chunk's start).
+  if (kI_new == nullptr || ((qp.p + 1) & (g.r - 1)) != 0) return;
+  constexpr int kPoolBatch = 64;
   const int j = qp.p >> g.log2r;
   const int past = g.past_len[qp.b], t0 = g.cu_q[qp.b];
   const int dI = g.dI;
   float acc = 0.0f;
-  for (int s0 = j << g.log2r; s0 <= qp.p; s0 += kStageRows) {
-    const int nrow = min(kStageRows, qp.p + 1 - s0);
-    for (int e = tid; e < nrow * dI; e += blockDim.x) {
-      const int rr = e / dI, x = e - rr * dI;
-      const int s = s0 + rr;
-      float v = 0.0f;
-      if (s >= past) {
-        v = to_f32(kI_new[(int64_t)(t0 + s - past) * dI + x]);
+  if (tid < dI) {
+    for (int s0 = j << g.log2r; s0 <= qp.p; s0 += kPoolBatch) {
+      const int n = qp.p + 1 - s0;  // rows left (the batch takes min(n, kPoolBatch))
+      float v[kPoolBatch];
+      if (s0 >= past) {
+        // all of the batch appended by this call: rows dI apart in kI_new
+        const E* src = kI_new + (int64_t)(t0 + s0 - past) * dI + tid;
+#pragma unroll
+        for (int i = 0; i < kPoolBatch; ++i) v[i] = to_f32(src[(int64_t)min(i, n - 1) * dI]);
       } else {
-        const int64_t row = idx_row(g, qp.b, s);
-        if (row >= 0) v = to_f32(kI_cache[row + x]);
+#pragma unroll 8
+        for (int i = 0; i < kPoolBatch; ++i) {
+          const int s = min(s0 + i, qp.p);
+          if (s >= past) {
+            v[i] = to_f32(kI_new[(int64_t)(t0 + s - past) * dI + tid]);
+          } else {
+            const int64_t row = idx_row(g, qp.b, s);
+            v[i] = row >= 0 ? to_f32(kI_cache[row + tid]) : 0.0f;
+          }
+        }
       }
-      stage[e] = v;
-    }
-    __syncthreads();
-    if (tid < dI) {
-      // (16 rows read at a time so the LDS reads overlap; adds in token order)
-      for (int r0 = 0; r0 < nrow; r0 += 16) {
-        float v[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = stage[min(r0 + i, nrow - 1) * dI + tid];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (r0 + i < nrow) acc = acc + v[i];
-      }
+      for (int i = 0; i < kPoolBatch; ++i)
+        if (i < n) acc = acc + v[i];
     }
-    __syncthreads();
   }
   float mean = acc * g.inv_r;
   if (g.idx_rope_dim > 0) {
@@ -1926,12 +1930,12 @@ hipError_t launch_append_pool(const Geo& g, int elem, const void* k_new, const v
                               float* pooled, const RopeTab& idx_rope, hipStream_t st) {
   if (g.T == 0) return hipSuccess;
   if (elem == kBF16) {
-    append_pool_kernel<uint16_t><<<g.T, 256, 0, st>>>(
+    append_pool_kernel<uint16_t><<<dim3(g.T, 2), 256, 0, st>>>(
         g, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
         static_cast<const uint16_t*>(kI_new), static_cast<uint16_t*>(k_cache),
         static_cast<uint16_t*>(v_cache), static_cast<uint16_t*>(kI_cache), pooled, idx_rope);
   } else {
-    append_pool_kernel<float><<<g.T, 256, 0, st>>>(
+    append_pool_kernel<float><<<dim3(g.T, 2), 256, 0, st>>>(
         g, static_cast<const float*>(k_new), static_cast<const float*>(v_new),
         static_cast<const float*>(kI_new), static_cast<float*>(k_cache),
         static_cast<float*>(v_cache), static_cast<float*>(kI_cache), pooled, idx_rope);
