@@ -269,25 +269,42 @@ __global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
 
 // 8-bit K/V in the rotated basis: each query row of the sub-batch rotated
 // once (q' = H q, the Sylvester Hadamard matrix in the standard butterfly
-// order) and rounded to bf16 for the matrix cores, as the decode kernel does
-// with its staged query.  One wave per (query, head) row: lane l holds dims
-// 2 l, 2 l + 1 (one stage in the lane, six across lanes).
+// order: dim bit 0 first) and rounded to bf16 for the matrix cores, as the
+// decode kernel does with its staged query.  16 lanes per (query, head) row,
+// 4 rows per wave: lane l16 holds dims 8 l16 .. +7 (16-byte loads and
+// stores), bits 0-2 of the dim in the lane, bits 3-6 across lanes.
 __global__ __launch_bounds__(256) void ks_rotate_q_kernel(Geo g, KsArgs a,
                                                          const uint16_t* __restrict__ q) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t - t_lo) * Hq + h
-  if (row >= (int64_t)(a.t_hi - a.t_lo) * g.Hq) return;  // whole wave
-  const uint32_t pr =
-      *reinterpret_cast<const uint32_t*>(q + ((int64_t)a.t_lo * g.Hq + row) * 128 + 2 * lane);
-  const float x = bf_lo(pr), y = bf_hi(pr);
-  float x0 = x + y, x1 = x - y;
+  const int lane = threadIdx.x & 63, l16 = lane & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (t - t_lo) * Hq + h
+  const bool ok = row < (int64_t)(a.t_hi - a.t_lo) * g.Hq;
+  const uint4 pr =
+      ok ? *reinterpret_cast<const uint4*>(q + ((int64_t)a.t_lo * g.Hq + row) * 128 + 8 * l16)
+         : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t pw[4] = {pr.x, pr.y, pr.z, pr.w};
+  float v[8];
 #pragma unroll
-  for (int dl = 1; dl < 64; dl <<= 1) {
-    const bool up = (lane & dl) != 0;
-    x0 = fwht_cross(x0, dl, up);
-    x1 = fwht_cross(x1, dl, up);
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf_lo(pw[i]);
+    v[2 * i + 1] = bf_hi(pw[i]);
   }
-  *reinterpret_cast<uint32_t*>(a.qrot + row * 128 + 2 * lane) = pack_bf16(x0, x1);
+#pragma unroll
+  for (int len = 1; len < 8; len <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (!(i & len)) {
+        const float x = v[i], y = v[i + len];
+        v[i] = x + y;
+        v[i + len] = x - y;
+      }
+#pragma unroll
+  for (int dl = 1; dl < 16; dl <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fwht_cross(v[i], dl, (l16 & dl) != 0);
+  if (ok)
+    *reinterpret_cast<uint4*>(a.qrot + row * 128 + 8 * l16) =
+        make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]),
+                   pack_bf16(v[6], v[7]));
 }
 
 // One workgroup (4 waves) per (work item, KV head).  Matrix-core layout of
@@ -726,7 +743,7 @@ hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const 
     const int n_items = (int)ks_item_slots(g, a.nr, a.t_hi - a.t_lo);
     a.n_items = n_items;
     if (a.qrot != nullptr)
-      ks_rotate_q_kernel<<<(int)(((int64_t)(a.t_hi - a.t_lo) * g.Hq + 3) / 4), 256, 0, st>>>(
+      ks_rotate_q_kernel<<<(int)(((int64_t)(a.t_hi - a.t_lo) * g.Hq + 15) / 16), 256, 0, st>>>(
           g, a, static_cast<const uint16_t*>(q));
     ks_count_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
     if (a.nb1 <= kScanThreads) ks_scan_kernel<1><<<g.B, kScanThreads, 0, st>>>(g, a);
