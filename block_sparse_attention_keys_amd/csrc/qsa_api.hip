@@ -714,6 +714,8 @@ int64_t qsa_probe_keys_visited(int32_t reset) {
   if (qsa::ks_keys_visited(&w, reset != 0) != hipSuccess) return -1;
   return (int64_t)(v + w);
 }
+
+void qsa_probe_library_gemm(int32_t enable) { qsa::lt_set_enabled(enable != 0); }
 #endif
 
 }  // extern "C"

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -45,6 +46,9 @@ struct LtDevice {
 };
 
 constexpr int kMaxDevices = 64;
+#ifdef QSA_COUNT_KEYS
+std::atomic<bool> g_off{false};  // (debug builds) hipBLASLt switched off by a test
+#endif
 std::mutex g_mu;
 bool g_api_tried = false;
 LtApi g_api;
@@ -102,8 +106,15 @@ LtPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, bool d_f32) {
 
 }  // namespace
 
+#ifdef QSA_COUNT_KEYS
+void lt_set_enabled(bool on) { g_off = !on; }
+#endif
+
 hipError_t lt_gemm(const void* A, const void* B, void* D, bool d_f32, int M, int N, int K,
                    hipStream_t st) {
+#ifdef QSA_COUNT_KEYS
+  if (g_off) return hipErrorNotSupported;
+#endif
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return hipErrorNotSupported;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;

@@ -120,6 +120,10 @@ hipError_t launch_proj_reduce(const float* part, int S, int64_t MN, void* out, h
 // when it cannot run the product (the caller then runs its own kernel).
 hipError_t lt_gemm(const void* A, const void* B, void* D, bool d_f32, int M, int N, int K,
                    hipStream_t st);
+#ifdef QSA_COUNT_KEYS
+// Debug builds: false makes lt_gemm decline every product (the tiled kernel runs).
+void lt_set_enabled(bool on);
+#endif
 hipError_t launch_block_prep(const Geo& g, const BlockPrepArgs& a, hipStream_t st);
 
 #ifdef QSA_COUNT_KEYS

@@ -104,6 +104,9 @@ def _load(path: str) -> C.CDLL:
     if hasattr(L, "qsa_probe_keys_visited"):
         L.qsa_probe_keys_visited.restype = C.c_int64
         L.qsa_probe_keys_visited.argtypes = [C.c_int32]
+    if hasattr(L, "qsa_probe_library_gemm"):
+        L.qsa_probe_library_gemm.restype = None
+        L.qsa_probe_library_gemm.argtypes = [C.c_int32]
     return L
 
 

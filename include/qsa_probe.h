@@ -22,6 +22,12 @@ extern "C" {
  * HIP error. */
 int64_t qsa_probe_keys_visited(int32_t reset);
 
+/* The block front end's prefill-sized projections run on hipBLASLt where it
+ * is present; enable = 0 makes them run the library's own LDS-tiled MFMA
+ * kernel instead (until called again with a non-zero value), so that tests
+ * cover both.  Process-wide; not thread-safe against running calls. */
+void qsa_probe_library_gemm(int32_t enable);
+
 #ifdef __cplusplus
 }
 #endif

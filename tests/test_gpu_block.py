@@ -216,6 +216,22 @@ def test_block_prefill_then_decode_paged():
         _check_block(bc, dc, res[i], sample=None if i >= last - 2 else 96, seed=i)
 
 
+def test_block_prefill_on_the_tiled_gemm():
+    """The block's prefill-sized projections on the library's own LDS-tiled
+    MFMA kernel (hipBLASLt switched off in the probe build), chunked prefill
+    and a decode step against the oracle."""
+    bc = workloads.make_block_case("ragged_paged_decode_128k_bf16", d_model=512, n_seqs=2,
+                                   ctx_range=(900, 4000), chunk=2048, decode_steps=1)
+    with qsa.probe_library() as P:
+        P.qsa_probe_library_gemm(0)
+        try:
+            dc, res = _run_block(bc)
+        finally:
+            P.qsa_probe_library_gemm(1)
+    for i in sorted(res):
+        _check_block(bc, dc, res[i], sample=64, seed=i)
+
+
 def test_block_contiguous_equals_paged_bitwise():
     bc = workloads.make_block_case("ragged_paged_decode_128k_bf16", d_model=256, n_seqs=3,
                                    ctx_range=(300, 2500), chunk=1024, decode_steps=2)
