@@ -546,15 +546,21 @@ __global__ __launch_bounds__(256, 3) void ks_attn_kernel(Geo g, KsArgs a,
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // (all four rows' indices and values read before the first store)
+    int orow[4];
+    uint4 ov[4];
+    const int ch = lane & 15;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rr = 4 * i + (lane >> 4), ch = lane & 15;
-      const int orow = __shfl(row, rr, 64);
-      const uint4 v = os[rr * 16 + (ch ^ rr)];
-      if (orow >= 0)
-        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v),
-                                    reinterpret_cast<u32x4_t*>(a.po + (int64_t)orow * D + 8 * ch));
+      const int rr = 4 * i + (lane >> 4);
+      orow[i] = __shfl(row, rr, 64);
+      ov[i] = os[rr * 16 + (ch ^ rr)];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (orow[i] >= 0)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, ov[i]),
+                                    reinterpret_cast<u32x4_t*>(a.po + (int64_t)orow[i] * D + 8 * ch));
     // (the next tile's writes to Os wait for these reads: in-order LDS
     // traffic of one wave)
     __builtin_amdgcn_wave_barrier();
