@@ -172,39 +172,61 @@ __global__ __launch_bounds__(256) void append_pool_kernel(
   // read from kI_new (another workgroup may not have stored them yet); older
   // rows come from the cache.  One thread per column adds the rows in token
   // order (the sequential fp32 sum); its loads go out kPoolBatch rows at a
-  // time, all requested before the first add when the batch lies in this
-  // call's rows (a block of a prefill chunk, except where it straddles the
-  // chunk's start).
+  // time, all requested before the first add (rows in the cache first have
+  // their addresses resolved, one thread per row).
   if (kI_new == nullptr || ((qp.p + 1) & (g.r - 1)) != 0) return;
   constexpr int kPoolBatch = 64;
   const int j = qp.p >> g.log2r;
   const int past = g.past_len[qp.b], t0 = g.cu_q[qp.b];
   const int dI = g.dI;
+  __shared__ const E* rowp[kPoolBatch];  // a batch's row starts (cache rows' lookups)
+  __shared__ int rowok[kPoolBatch];
   float acc = 0.0f;
-  if (tid < dI) {
-    for (int s0 = j << g.log2r; s0 <= qp.p; s0 += kPoolBatch) {
-      const int n = qp.p + 1 - s0;  // rows left (the batch takes min(n, kPoolBatch))
-      float v[kPoolBatch];
-      if (s0 >= past) {
-        // all of the batch appended by this call: rows dI apart in kI_new
+  for (int s0 = j << g.log2r; s0 <= qp.p; s0 += kPoolBatch) {  // uniform
+    const int n = qp.p + 1 - s0;  // rows left (the batch takes min(n, kPoolBatch))
+    if (s0 >= past) {
+      // all of the batch appended by this call: rows dI apart in kI_new
+      if (tid < dI) {
         const E* src = kI_new + (int64_t)(t0 + s0 - past) * dI + tid;
+        float v[kPoolBatch];
 #pragma unroll
         for (int i = 0; i < kPoolBatch; ++i) v[i] = to_f32(src[(int64_t)min(i, n - 1) * dI]);
-      } else {
-#pragma unroll 8
-        for (int i = 0; i < kPoolBatch; ++i) {
-          const int s = min(s0 + i, qp.p);
-          if (s >= past) {
-            v[i] = to_f32(kI_new[(int64_t)(t0 + s - past) * dI + tid]);
-          } else {
-            const int64_t row = idx_row(g, qp.b, s);
-            v[i] = row >= 0 ? to_f32(kI_cache[row + tid]) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < kPoolBatch; ++i)
+          if (i < n) acc = acc + v[i];
+      }
+    } else {
+      // rows in the cache: one thread per row resolves its address (page
+      // lookups all at once); absent rows read the token's own row, unused
+      if (tid < kPoolBatch) {
+        const int s = min(s0 + tid, qp.p);
+        const E* ptr = kI_new + (int64_t)t * dI;
+        int ok = tid < n;
+        if (s >= past) {
+          ptr = kI_new + (int64_t)(t0 + s - past) * dI;
+        } else {
+          const int64_t row = idx_row(g, qp.b, s);
+          if (row >= 0) ptr = kI_cache + row;
+          else ok = 0;
+        }
+        rowp[tid] = ptr;
+        rowok[tid] = ok;
+      }
+      __syncthreads();
+      if (tid < dI) {
+        for (int c0 = 0; c0 < kPoolBatch && c0 < n; c0 += 16) {  // 16 loads in flight
+          float v[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x = to_f32(rowp[c0 + i][tid]);
+            v[i] = rowok[c0 + i] ? x : 0.0f;
           }
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (c0 + i < n) acc = acc + v[i];
         }
       }
-#pragma unroll
-      for (int i = 0; i < kPoolBatch; ++i)
-        if (i < n) acc = acc + v[i];
+      __syncthreads();  // the next batch rewrites rowp
     }
   }
   float mean = acc * g.inv_r;
