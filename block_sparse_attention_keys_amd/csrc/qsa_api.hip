@@ -716,6 +716,13 @@ int64_t qsa_probe_keys_visited(int32_t reset) {
 }
 
 void qsa_probe_library_gemm(int32_t enable) { qsa::lt_set_enabled(enable != 0); }
+
+int32_t qsa_probe_gemm(const void* A, const void* B, void* D, int32_t d_f32, int32_t M, int32_t N,
+                       int32_t K, void* stream) {
+  if (A == nullptr || B == nullptr || D == nullptr || M <= 0 || N <= 0 || K <= 0) return -1;
+  const hipError_t e = qsa::lt_gemm(A, B, D, d_f32 != 0, M, N, K, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : (e == hipErrorNotSupported ? 1 : -1);
+}
 #endif
 
 }  // extern "C"

@@ -23,6 +23,8 @@ namespace {
 struct LtApi {
   decltype(&hipblasLtCreate) create = nullptr;
   decltype(&hipblasLtMatmulDescCreate) desc_create = nullptr;
+  decltype(&hipblasLtMatmulDescDestroy) desc_destroy = nullptr;
+  decltype(&hipblasLtMatrixLayoutDestroy) layout_destroy = nullptr;
   decltype(&hipblasLtMatmulDescSetAttribute) desc_set = nullptr;
   decltype(&hipblasLtMatrixLayoutCreate) layout_create = nullptr;
   decltype(&hipblasLtMatmulPreferenceCreate) pref_create = nullptr;
@@ -46,6 +48,11 @@ struct LtDevice {
 };
 
 constexpr int kMaxDevices = 64;
+// Plans kept per device (one per product shape; the token count varies from
+// call to call): past this many the cache is emptied and rebuilt on demand.
+// The heuristic picks the same algorithm for a shape every time, so the
+// kernel a shape runs does not depend on the calls before it.
+constexpr size_t kMaxPlans = 64;
 #ifdef QSA_COUNT_KEYS
 std::atomic<bool> g_off{false};  // (debug builds) hipBLASLt switched off by a test
 #endif
@@ -63,6 +70,8 @@ bool load_api() {
   LtApi a;
   a.create = reinterpret_cast<decltype(a.create)>(dlsym(so, "hipblasLtCreate"));
   a.desc_create = reinterpret_cast<decltype(a.desc_create)>(dlsym(so, "hipblasLtMatmulDescCreate"));
+  a.desc_destroy = reinterpret_cast<decltype(a.desc_destroy)>(dlsym(so, "hipblasLtMatmulDescDestroy"));
+  a.layout_destroy = reinterpret_cast<decltype(a.layout_destroy)>(dlsym(so, "hipblasLtMatrixLayoutDestroy"));
   a.desc_set = reinterpret_cast<decltype(a.desc_set)>(dlsym(so, "hipblasLtMatmulDescSetAttribute"));
   a.layout_create = reinterpret_cast<decltype(a.layout_create)>(dlsym(so, "hipblasLtMatrixLayoutCreate"));
   a.pref_create = reinterpret_cast<decltype(a.pref_create)>(dlsym(so, "hipblasLtMatmulPreferenceCreate"));
@@ -70,8 +79,9 @@ bool load_api() {
   a.pref_destroy = reinterpret_cast<decltype(a.pref_destroy)>(dlsym(so, "hipblasLtMatmulPreferenceDestroy"));
   a.heuristic = reinterpret_cast<decltype(a.heuristic)>(dlsym(so, "hipblasLtMatmulAlgoGetHeuristic"));
   a.matmul = reinterpret_cast<decltype(a.matmul)>(dlsym(so, "hipblasLtMatmul"));
-  if (!a.create || !a.desc_create || !a.desc_set || !a.layout_create || !a.pref_create ||
-      !a.pref_set || !a.pref_destroy || !a.heuristic || !a.matmul)
+  if (!a.create || !a.desc_create || !a.desc_destroy || !a.desc_set || !a.layout_create ||
+      !a.layout_destroy || !a.pref_create || !a.pref_set || !a.pref_destroy || !a.heuristic ||
+      !a.matmul)
     return false;
   g_api = a;
   return true;
@@ -104,6 +114,17 @@ LtPlan make_plan(hipblasLtHandle_t h, int M, int N, int K, bool d_f32) {
   return p;
 }
 
+void free_plans(LtDevice& L) {
+  for (auto& kv : L.plans) {
+    LtPlan& p = kv.second;
+    if (p.la != nullptr) g_api.layout_destroy(p.la);
+    if (p.lb != nullptr) g_api.layout_destroy(p.lb);
+    if (p.ld != nullptr) g_api.layout_destroy(p.ld);
+    if (p.desc != nullptr) g_api.desc_destroy(p.desc);
+  }
+  L.plans.clear();
+}
+
 }  // namespace
 
 #ifdef QSA_COUNT_KEYS
@@ -131,6 +152,7 @@ hipError_t lt_gemm(const void* A, const void* B, void* D, bool d_f32, int M, int
       if (g_api.create(&L.h) != HIPBLAS_STATUS_SUCCESS) L.h = nullptr;
     }
     if (L.h == nullptr) return hipErrorNotSupported;
+    if (L.plans.size() >= kMaxPlans) free_plans(L);
     it = L.plans.emplace(key, make_plan(L.h, M, N, K, d_f32)).first;
   }
   const LtPlan& p = it->second;

@@ -107,6 +107,9 @@ def _load(path: str) -> C.CDLL:
     if hasattr(L, "qsa_probe_library_gemm"):
         L.qsa_probe_library_gemm.restype = None
         L.qsa_probe_library_gemm.argtypes = [C.c_int32]
+    if hasattr(L, "qsa_probe_gemm"):
+        L.qsa_probe_gemm.restype = C.c_int32
+        L.qsa_probe_gemm.argtypes = [vp, vp, vp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, vp]
     return L
 
 

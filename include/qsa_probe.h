@@ -28,6 +28,15 @@ int64_t qsa_probe_keys_visited(int32_t reset);
  * cover both.  Process-wide; not thread-safe against running calls. */
 void qsa_probe_library_gemm(int32_t enable);
 
+/* One product D[M][N] = A[M][K] B[N][K]^T (bf16 inputs, row-major; D fp32
+ * when d_f32, else bf16) through the library's hipBLASLt path, enqueued on
+ * `stream` (a hipStream_t; NULL = the null stream).  Device pointers.
+ * Returns 0 when enqueued, 1 when hipBLASLt cannot run it (missing, no
+ * algorithm, or stream capture before the shape has a plan), -1 on bad
+ * arguments or a failed launch. */
+int32_t qsa_probe_gemm(const void* A, const void* B, void* D, int32_t d_f32, int32_t M, int32_t N,
+                       int32_t K, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

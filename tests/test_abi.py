@@ -242,15 +242,15 @@ PROBE_HEADER = os.path.join(ROOT, "include", "qsa_probe.h")
 
 
 def test_probe_symbols_only_in_the_probe_build(L):
-    """include/qsa_probe.h: the row counter and the GEMM-library switch exist
-    in libqsa_probe.so only; the probe build exports the whole boundary as
-    well."""
+    """include/qsa_probe.h: the row counter, the GEMM-library switch and the
+    direct library product exist in libqsa_probe.so only; the probe build
+    exports the whole boundary as well."""
     if not os.path.exists(qsa.PROBE_PATH):
         from block_sparse_attention_keys_amd import build
         build.build(build.PROBE_LIB, build.PROBE_FLAGS)
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     probe_names = sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", text)))
-    assert probe_names == ["qsa_probe_keys_visited", "qsa_probe_library_gemm"]
+    assert probe_names == ["qsa_probe_gemm", "qsa_probe_keys_visited", "qsa_probe_library_gemm"]
     P = C.CDLL(qsa.PROBE_PATH)
     for n in probe_names:
         assert hasattr(P, n), n
