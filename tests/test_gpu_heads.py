@@ -2,8 +2,8 @@
 query heads per KV head; the attention kernels are instantiated for 1, 2, 4,
 8 and 16, and the prefill kernel places its workgroups by KV head when Hkv
 divides the 8 XCDs (and falls back to a plain order otherwise).  Each
-grouping runs a ragged paged decode and a chunked prefill large enough for
-the MFMA prefill kernel, against the CPU oracle."""
+grouping runs a ragged paged decode, a chunked prefill on the key-stationary
+path and one on the per-token MFMA prefill kernel, against the CPU oracle."""
 import dataclasses
 
 import pytest
@@ -45,10 +45,25 @@ def test_decode_head_groupings(hq, hkv):
 
 @pytest.mark.parametrize("hq,hkv", HEADS)
 def test_mfma_prefill_head_groupings(hq, hkv):
-    """600-token chunks: at least 600 (token, KV head) units per call, so the
-    MFMA prefill kernel runs (a ragged last chunk included)."""
+    """600-token chunks of one sequence: the key-stationary path (a sequence
+    with at least 512 new tokens), then a ragged 37-token chunk."""
     case = _case("chunked_prefill_32k_bf16", hq, hkv, prefill_len=2 * 600 + 37, chunk=600)
     say(f"prefill Hq={hq} Hkv={hkv} calls={len(case.calls)}")
+    dc = runner.DeviceCase(case)
+    res = run_calls(dc)
+    seqf = SeqF32(case)
+    for i in sorted(res):
+        check_call(dc, seqf, res[i], sample=48, rng_seed=i)
+
+
+@pytest.mark.parametrize("hq,hkv", HEADS)
+def test_per_token_mfma_prefill_head_groupings(hq, hkv):
+    """Two sequences of 300-token chunks: 600 tokens per call, at least 512
+    (token, KV head) units and no sequence with 512 new tokens, so the
+    per-token MFMA prefill kernel runs."""
+    case = _case("chunked_prefill_32k_bf16", hq, hkv, n_seqs=2, prefill_len=2 * 300 + 37,
+                 chunk=300)
+    say(f"per-token prefill Hq={hq} Hkv={hkv} calls={len(case.calls)}")
     dc = runner.DeviceCase(case)
     res = run_calls(dc)
     seqf = SeqF32(case)

@@ -369,3 +369,17 @@ def test_prefill_key_stationary_many_candidate_blocks(n_tok):
     case = workloads._draw(sp, 0)
     case.calls = [[(0, n_tok - 1024)], [(n_tok - 1024, n_tok)]]
     _full(case, sample=24)
+
+
+def test_prefill_key_stationary_block_128():
+    """Block size 128 with the 256K decode's heads (Hq 32, Hkv 4, indexer
+    8 x 64, budget 4096: k = 32) through the key-stationary prefill, whose
+    128-key blocks fill the LDS; 2048-token chunks, the last ragged, with
+    more candidate blocks than k in the later chunks."""
+    import dataclasses
+    sp = dataclasses.replace(workloads.SPECS["chunked_prefill_32k_bf16"], n_q_heads=32,
+                             n_kv_heads=4, n_idx_heads=8, block_size=128, budget=4096,
+                             prefill_len=6000, chunk=2048)
+    case = workloads._draw(sp, 0)
+    _full(case, sample=48)
+    _full(case, sample=48, layout="paged")
