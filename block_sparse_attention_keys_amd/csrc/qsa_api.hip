@@ -1,7 +1,9 @@
 // C ABI of the QSA hot path: argument validation, workspace layout and launch
 // sequencing.  No arithmetic of the method happens here; every step runs in
-// the kernels of qsa_kernels.hip and qsa_block.hip.  (The host fills only the
-// rotary frequency tables, theta^(-2i/R) in fp64 with the C library's pow.)
+// the kernels of qsa_kernels.hip, qsa_prefill_ks.hip and qsa_block.hip (and,
+// for the block's prefill-sized projections, hipBLASLt: qsa_blas.hip).  (The
+// host fills only the rotary frequency tables, theta^(-2i/R) in fp64 with the
+// C library's pow.)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
@@ -15,7 +17,8 @@
 #include "qsa_internal.h"
 
 // Device scratch of qsa_forward_noalloc: its workspace (scores, selections,
-// split partials) for callers that cannot allocate.  Every GPU the library
+// split partials, key-stationary plan and partial states) for callers that
+// cannot allocate.  Every GPU the library
 // runs on holds one copy until the process ends.  Host code never passes the
 // array's name to a kernel (on the host it is only a stand-in for the symbol):
 // it uses the per-device address hipGetSymbolAddress returns.

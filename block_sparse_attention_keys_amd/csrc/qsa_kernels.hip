@@ -3,10 +3,12 @@
 // Kernels (one QSA layer step):
 //   append_pool   write new K/V/indexer-key rows at each sequence's past_len and
 //                 pool every block the new tokens complete (mean of r indexer
-//                 keys, fp32, tokens ascending).
-//   score         relu-weighted multi-head block scores, one lane per 4 blocks,
+//                 keys, fp32, tokens ascending), pooling in workgroups of its
+//                 own dispatched ahead of the copies.
+//   score         relu-weighted multi-head block scores, one lane per block,
 //                 fp32 fmaf chains in a fixed order (the order is what makes the
-//                 selection reproducible bit for bit).
+//                 selection reproducible bit for bit); its decode form also
+//                 appends and pools (at most one new token per sequence).
 //   select        per-query top-k by (score desc, index asc): 4-pass 8-bit radix
 //                 select in LDS, then an ascending compaction.
 //   attn_decode   gated GQA softmax attention over the selected blocks + tail
@@ -14,7 +16,9 @@
 //                 splits of the selection list, QK and PV on bf16 MFMA, the
 //                 top-k made in the kernel when it is given the scores.
 //   attn_prefill_mfma  the same for prefill-sized calls: one wave per (token,
-//                 KV head), QK and PV on bf16 MFMA.
+//                 KV head), QK and PV on bf16 MFMA (calls where some sequence has
+//                 512 or more new tokens take the key-stationary path of
+//                 qsa_prefill_ks.hip instead).
 //   attn_split    the generic form (fp32, D = 64): one wave per (token, KV
 //                 head, split); online softmax in base 2.
 //   attn_combine  log-sum-exp merge of the splits and the sigmoid output gate.

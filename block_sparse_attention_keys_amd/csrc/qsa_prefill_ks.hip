@@ -15,11 +15,17 @@
 //              head) rows at a time as dense bf16 MFMA tiles, S^T = K Q^T
 //              then O^T = V^T P^T, with a causal mask per row (the tail block
 //              of a query is partial).  Each row's partial state is stored:
-//              its output normalised by its own sum (bf16) and its base-2
+//              its output normalised by its own sum (bf16; whole 128-byte
+//              lines, through an LDS exchange inside the wave) and its base-2
 //              log-sum-exp (fp32), at (query, slot, head).
 //   ks_merge   per (query, 16 heads), the log-sum-exp merge of the query's
 //              slots (its selected blocks, then the tail), then the sigmoid
-//              gate.
+//              gate (and, for 8-bit caches in the rotated basis, the inverse
+//              rotation and the V scale).
+//   ks_rotate_q  8-bit caches in the rotated basis: each query row rotated
+//              once per sub-batch, for the attention's query operand.
+// Calls with more than kKsSubTokens new tokens run in sub-batches of that
+// many queries (the partial states of one sub-batch at a time).
 //
 // The attention is the one of the pages' QSA description (MTPLX "Native
 // Backend Components", section "Qwen Sparse Attention": standard gated GQA
