@@ -77,7 +77,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the QSA hot path "
-                                   "has no multi-GPU leg (see DESIGN.md, sharding)",
+                                   "has no multi-GPU leg (it would shard by sequence, KV head "
+                                   "or context; none of these is built)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
