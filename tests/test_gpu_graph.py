@@ -1,9 +1,10 @@
 """The calls are graph-capturable: no allocation, no host synchronisation,
-no memset or copy nodes.  A decode step (qsa_forward) and a block step
-(qsa_block_forward) are captured into a HIP graph through torch, replayed
-several times with eager work and synchronisations in between, and every
-replay must reproduce the eager call bit for bit (the step rewrites the
-same cache rows with the same values, so replays are idempotent)."""
+no memset or copy nodes.  Decode and prefill steps of the path (qsa_forward)
+and of the block (qsa_block_forward) are captured into a HIP graph through
+torch, replayed several times with eager work and synchronisations in
+between, and every replay must reproduce the eager call bit for bit (the
+step rewrites the same cache rows with the same values, so replays are
+idempotent)."""
 import numpy as np
 import pytest
 import torch
@@ -77,5 +78,21 @@ def test_block_decode_step_graph():
     dc = runner.BlockDeviceCase(bc)
     dc.forward(dc.call_inputs(0))      # the context, through the block
     c = dc.call_inputs(1)
+    outs = {"y": c["y"], "sel": c["sel"], "n_blocks": c["n_blocks"]}
+    _replays_match(lambda: dc.forward(c), outs)
+
+
+def test_block_prefill_chunk_graph():
+    """A 2048-token block prefill step: its projections go through hipBLASLt
+    (the plan was made by the eager call of the same shape before capture) and
+    its attention through the key-stationary plan, attention and merge."""
+    bc = workloads.make_block_case("ragged_paged_decode_128k_bf16", d_model=512, n_seqs=2,
+                                   ctx_range=(2500, 3500), chunk=1024, decode_steps=1)
+    dc = runner.BlockDeviceCase(bc)
+    first = dc.call_inputs(0)
+    assert first["T"] == 2048
+    dc.forward(first)
+    c = dc.call_inputs(1)
+    assert c["T"] == 2048
     outs = {"y": c["y"], "sel": c["sel"], "n_blocks": c["n_blocks"]}
     _replays_match(lambda: dc.forward(c), outs)
