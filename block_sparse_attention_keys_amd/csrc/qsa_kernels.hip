@@ -7,8 +7,11 @@
 //                 own dispatched ahead of the copies.
 //   score         relu-weighted multi-head block scores, one lane per block,
 //                 fp32 fmaf chains in a fixed order (the order is what makes the
-//                 selection reproducible bit for bit); its decode form also
-//                 appends and pools (at most one new token per sequence).
+//                 selection reproducible bit for bit): score_tile for calls
+//                 with many new tokens (a resident grid, each wave a range of
+//                 consecutive tokens, the query as scalar operands); the decode
+//                 form of score_kernel also appends and pools (at most one new
+//                 token per sequence).
 //   select        per-query top-k by (score desc, index asc): 4-pass 8-bit radix
 //                 select in LDS, then an ascending compaction.
 //   attn_decode   gated GQA softmax attention over the selected blocks + tail
@@ -500,6 +503,118 @@ __global__ __launch_bounds__(64) void score_kernel(
     }
   }
   if (j < g.nbcap && j != jnew) scores[(int64_t)t * g.nbcap + j] = (j < nb) ? s : -INFINITY;
+}
+
+// score, the form for calls that bring many tokens at once (prefill chunks,
+// ragged prefill, verify).  The work is T x ceil(nbcap / 64) units (token,
+// group of 64 candidate blocks), group-major; a grid of as many 4-wave
+// workgroups as the GPU holds at once gives every wave an equal contiguous
+// range of units (the counts differ by at most one), so no wave waits for a
+// second round and a wave's tokens are consecutive within a group.  Lanes
+// are the group's blocks; a sequence's pooled keys are loaded into registers
+// once for all of its tokens in the range.  A token's query and head weights
+// are the same for every lane, so they are read with scalar loads and enter
+// each fmaf as its scalar operand (broadcasting them through LDS would move
+// 256 bytes per value and wave, more than the LDS delivers for one fmaf per
+// lane and value).  Every score is the same fmaf chain as the per-token form
+// (x ascending per head, then heads ascending).
+template <typename E, int HIM, int DI>
+__global__ __launch_bounds__(256) void score_tile_kernel(Geo g, const E* __restrict__ qI,
+                                                         const float* __restrict__ w,
+                                                         const float* __restrict__ pooled,
+                                                         float* __restrict__ scores) {
+  __shared__ int tinfo[4][64][2];  // (sequence, complete blocks) of up to 64 tokens
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int64_t T = g.T, groups = (g.nbcap + 63) / 64, U = T * groups;
+  const int64_t nw = (int64_t)gridDim.x * 4, gw = (int64_t)blockIdx.x * 4 + wv;
+  const int64_t u_end = (gw + 1) * U / nw;
+  const int HI = g.HI;
+  float pk[DI];
+  int kb = -1, kg = -1;  // sequence and group whose keys pk holds
+  for (int64_t u = gw * U / nw; u < u_end;) {
+    const int group = (int)(u / T), t0 = (int)(u - (int64_t)group * T);
+    const int nt = (int)min<int64_t>(min<int64_t>(u_end - u, T - t0), 64);
+    const int j = group * 64 + lane;
+    // Positions of the next nt tokens, one lane per token: the first one's
+    // sequence by search (the whole wave), then each lane steps over the
+    // sequence boundaries up to its token.
+    const QueryPos q0 = query_pos(g, t0);
+    wave_sync();  // (the previous tokens' entries have been read)
+    if (lane < nt) {
+      const int t = t0 + lane;
+      int b = g.one_q ? t : q0.b;
+      if (!g.one_q)
+        while (b + 1 < g.B && g.cu_q[b + 1] <= t) ++b;
+      const int p = g.one_q ? g.past_len[t] : g.past_len[b] + (t - g.cu_q[b]);
+      const bool ok = p >= 0 && p < g.cap;
+      tinfo[wv][lane][0] = b;
+      tinfo[wv][lane][1] = ok ? ((p + 1) >> g.log2r) : 0;
+    }
+    wave_sync();
+    for (int i = 0; i < nt; ++i) {
+      const int t = t0 + i;
+      const int b = __builtin_amdgcn_readfirstlane(tinfo[wv][i][0]);
+      const int nb = __builtin_amdgcn_readfirstlane(tinfo[wv][i][1]);
+      float s = 0.0f;
+      if (group * 64 < nb) {
+        if (b != kb || group != kg) {
+          const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(pooled + (int64_t)b * DI * g.pooled_ld,
+                                                        (uint32_t)(DI * g.pooled_ld * 4));
+          const uint32_t col = (uint32_t)min(j, g.pooled_ld - 1) * 4u;
+#pragma unroll
+          for (int x = 0; x < DI; ++x)
+            pk[x] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                  rs, col, (uint32_t)(x * g.pooled_ld * 4), 0));
+          kb = b;
+          kg = group;
+          // All key loads complete here, so the chains below carry no
+          // per-use waits for loads that only this branch issues.
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        // The query words of HB heads are requested together (at most 32
+        // scalar registers) and waited for once; the head weights first.
+        constexpr int DW = DI * (int)sizeof(E) / 4;  // 32-bit words per head row
+        constexpr int HB = DW >= 32 ? 1 : (32 / DW < HIM ? 32 / DW : HIM);
+        float wh[HIM];
+#pragma unroll
+        for (int h = 0; h < HIM; ++h) wh[h] = w[(int64_t)t * HI + min(h, HI - 1)];
+        const uint32_t* qt = reinterpret_cast<const uint32_t*>(qI) + (int64_t)t * HI * DW;
+#pragma unroll
+        for (int h0 = 0; h0 < HIM; h0 += HB) {
+          if (h0 < HI) {
+            uint32_t qw[HB][DW];
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+              for (int wd = 0; wd < DW; ++wd) qw[hh][wd] = qt[min(h0 + hh, HI - 1) * DW + wd];
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh) {
+              if (h0 + hh < HI) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int wd = 0; wd < DW; ++wd) {
+                  const uint32_t qd = qw[hh][wd];
+                  if constexpr (sizeof(E) == 2) {
+                    // bf16 pairs: the low half is the even dimension
+                    acc = fmaf(__builtin_bit_cast(float, qd << 16), pk[2 * wd], acc);
+                    acc = fmaf(__builtin_bit_cast(float, qd & 0xffff0000u), pk[2 * wd + 1], acc);
+                  } else {
+                    acc = fmaf(__builtin_bit_cast(float, qd), pk[wd], acc);
+                  }
+                }
+                float a = g.idx_scale * acc;
+                a = (a > 0.0f) ? a : 0.0f;
+                s = fmaf(wh[h0 + hh], a, s);
+              }
+            }
+          }
+        }
+      }
+      if (j < g.nbcap) scores[(int64_t)t * g.nbcap + j] = (j < nb) ? s : -INFINITY;
+    }
+    u += nt;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1906,6 +2021,27 @@ hipError_t attend_g(const Geo& g, const AttnPlan& plan, const void* q, const voi
   }
 }
 
+// The many-token scorer's grid: as many workgroups as the GPU holds at once
+// (from the kernel's occupancy, once per instantiation), or fewer when there
+// are fewer units than waves.
+template <typename E, int HIM, int DI>
+void score_tile_launch(const Geo& g, const E* q, const float* w, const float* pooled,
+                       float* scores, hipStream_t st) {
+  static const int resident = [] {
+    int dev = 0, per_cu = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, score_tile_kernel<E, HIM, DI>, 256,
+                                                     0) != hipSuccess ||
+        per_cu < 1)
+      return 1024;
+    return per_cu * prop.multiProcessorCount;
+  }();
+  const int64_t units = (int64_t)g.T * std::max(1, (g.nbcap + 63) / 64);
+  const int64_t wgs = std::min<int64_t>(resident, (units + 3) / 4);
+  score_tile_kernel<E, HIM, DI><<<(unsigned)wgs, 256, 0, st>>>(g, q, w, pooled, scores);
+}
+
 template <typename E, int DI, int MODE>
 void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float* scores,
               const AppendArgs& ap, const RopeTab& rt, hipStream_t st) {
@@ -1918,7 +2054,11 @@ void score_hd(const Geo& g, const void* qI, const float* w, float* pooled, float
   E* kc = static_cast<E*>(ap.k_cache);
   E* vc = static_cast<E*>(ap.v_cache);
   E* ic = static_cast<E*>(ap.kI_cache);
-  if (g.HI <= 4) {
+  if constexpr (MODE == 0) {
+    if (g.HI <= 4) score_tile_launch<E, 4, DI>(g, q, w, pooled, scores, st);
+    else if (g.HI <= 8) score_tile_launch<E, 8, DI>(g, q, w, pooled, scores, st);
+    else score_tile_launch<E, 16, DI>(g, q, w, pooled, scores, st);
+  } else if (g.HI <= 4) {
     score_kernel<E, 4, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic, rt);
   } else if (g.HI <= 8) {
     score_kernel<E, 8, DI, MODE><<<grid, 64, 0, st>>>(g, q, w, pooled, scores, kn, vn, in, kc, vc, ic, rt);
