@@ -883,6 +883,112 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restr
   if (tid == 0) n_blocks[t] = min(k, nb);
 }
 
+// select, up to 512 candidate blocks: one wave per query, four queries per
+// workgroup, lane l owning candidates [8 l, 8 l + 8).  The same 8-bit radix
+// passes and the same tie rule as block_radix_topk, on a histogram of the
+// wave's own in LDS: no workgroup barrier anywhere, so the calls with many
+// queries (prefill) keep four times as many selections in flight per CU as
+// with a workgroup per query.  A wave's LDS operations complete in the order
+// it issues them; the wavefront-scope fences keep the compiler from moving
+// them across the phase boundaries and wait for them to complete.
+constexpr int kSelectWaveBlocks = 512;
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+__global__ __launch_bounds__(256) void select_wave_kernel(Geo g, const float* __restrict__ scores,
+                                                          int32_t* __restrict__ sel,
+                                                          int32_t* __restrict__ n_blocks) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist_all[4][256];
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, k = g.k;
+  const int t = blockIdx.x * 4 + wid;
+  if (t >= g.T) return;  // (whole waves; no workgroup barrier follows)
+  uint32_t* hc = hist_all[wid];
+  const float* srow = scores + (int64_t)t * g.nbcap;
+  const int jb = 8 * lane;
+  // Unconditional loads at clamped indices, masked after with an AND (a
+  // select would let the compiler move each load under its own branch and
+  // wait for it there).
+  uint32_t kr[8];
+  const int jlast = max(g.nbcap - 1, 0);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = srow[min(jb + e, jlast)];
+    kr[e] = score_key(v) & (0u - (uint32_t)(jb + e < g.nbcap));
+  }
+  const QueryPos qp = query_pos(g, t);
+  const int nb = qp.ok ? min((qp.p + 1) >> g.log2r, g.nbcap) : 0;
+  int32_t* out = sel + (int64_t)t * k;
+  if (lane == 0) n_blocks[t] = min(k, nb);
+  if (nb <= k) {  // every candidate is kept
+    for (int i = lane; i < k; i += 64) out[i] = i < nb ? i : -1;
+    return;
+  }
+  const int jn = max(0, min(8, nb - jb));
+  uint32_t prefix = 0, mask = 0;
+  int want = k;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    *reinterpret_cast<uint4*>(&hc[4 * lane]) = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_sync();
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (e < jn && (kr[e] & mask) == prefix) atomicAdd(&hc[(kr[e] >> shift) & 255u], 1u);
+    wave_lds_sync();
+    // lane owns digits 255-4*lane .. 252-4*lane (descending)
+    const uint4 h4 = *reinterpret_cast<const uint4*>(&hc[252 - 4 * lane]);
+    wave_lds_sync();
+    const int c[4] = {(int)h4.w, (int)h4.z, (int)h4.y, (int)h4.x};
+    int above = wave_excl_scan(c[0] + c[1] + c[2] + c[3]);
+    int hit = 0, n_want = 0, n_cnt = 0;
+    uint32_t n_prefix = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (above < want && above + c[i] >= want) {
+        hit = 1;
+        n_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
+        n_want = want - above;
+        n_cnt = c[i];
+      }
+      above += c[i];
+    }
+    // exactly one lane holds the digit (nb > k keys were counted in pass 0,
+    // and every later pass counts the want-th key's digit group)
+    const int src = __builtin_ctzll(__ballot(hit));
+    prefix = (uint32_t)__builtin_amdgcn_readlane((int)n_prefix, src);
+    want = __builtin_amdgcn_readlane(n_want, src);
+    const int cnt = __builtin_amdgcn_readlane(n_cnt, src);
+    mask |= 255u << shift;
+    if (cnt == want) break;
+  }
+  // Keys above the found digits, and the first `want` keys that share them in
+  // index order: one packed scan gives each lane both counts.
+  int n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < jn) {
+      const uint32_t km = kr[e] & mask;
+      n_gt += km > prefix ? 1 : 0;
+      n_eq += km == prefix ? 1 : 0;
+    }
+  }
+  const int before = wave_excl_scan((n_gt << 16) | n_eq);
+  int pos = (before >> 16) + min(before & 0xffff, want);
+  int eqr = before & 0xffff;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < jn) {
+      const uint32_t km = kr[e] & mask;
+      const bool eq = km == prefix;
+      if (km > prefix || (eq && eqr < want)) {
+        if (pos < k) out[pos] = jb + e;
+        ++pos;
+      }
+      eqr += eq ? 1 : 0;
+    }
+  }
+}
+
 // select, more candidate blocks: one 256-thread workgroup per query, 8-bit
 // radix passes over the scores in memory.
 __global__ __launch_bounds__(256) void select_large_kernel(Geo g, const float* __restrict__ scores,
@@ -2129,7 +2235,9 @@ hipError_t launch_score_append(const Geo& g, int elem, const void* qI, const flo
 hipError_t launch_select(const Geo& g, const float* scores, int32_t* sel, int32_t* n_blocks,
                          hipStream_t st) {
   if (g.T == 0) return hipSuccess;
-  if (g.nbcap <= kSelectMaxBlocks) select_kernel<<<g.T, 256, 0, st>>>(g, scores, sel, n_blocks);
+  if (g.nbcap <= kSelectWaveBlocks)
+    select_wave_kernel<<<(g.T + 3) / 4, 256, 0, st>>>(g, scores, sel, n_blocks);
+  else if (g.nbcap <= kSelectMaxBlocks) select_kernel<<<g.T, 256, 0, st>>>(g, scores, sel, n_blocks);
   else select_large_kernel<<<g.T, 256, 0, st>>>(g, scores, sel, n_blocks);
   return hipGetLastError();
 }

@@ -172,6 +172,33 @@ def test_selection_ties_at_the_boundary():
     _full(case)
 
 
+def test_prefill_selection_ties_all_scores_equal():
+    """The prefill form of the all-equal case: zero indexer queries over a
+    chunked prefill whose later queries have more candidate blocks than k,
+    so the selection of those queries is the tie rule alone."""
+    case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=4096 + 37, chunk=1024)
+    for b in range(case.spec.n_seqs):
+        case.qI[b][:] = 0
+    _full(case)
+
+
+def test_prefill_selection_ties_at_the_boundary():
+    """The prefill form of the boundary tie: five blocks share one positive
+    score, all others score 0, and k = 32 lies inside the zeros."""
+    case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=4096 + 37, chunk=1024)
+    r = case.spec.block_size
+    for b in range(case.spec.n_seqs):
+        kI = workloads.as_f32(case.kI[b]).copy()
+        kI[:, 0] = -1.0
+        for blk in (3, 10, 40, 51, 60):
+            kI[blk * r:(blk + 1) * r, 0] = 1.0
+        case.kI[b] = workloads.bf16_bits(kI)
+        qI = np.zeros(case.qI[b].shape, np.float32)
+        qI[..., 0] = 1.0
+        case.qI[b] = workloads.bf16_bits(qI)
+    _full(case)
+
+
 # ----------------------------------------------------------------- the pages' case
 def test_pages_worked_count_released_config():
     """kv_len 3002, ratio 4, budget 2048: 512 of 750 blocks and 2050 keys
