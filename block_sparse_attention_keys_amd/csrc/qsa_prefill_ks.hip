@@ -9,7 +9,9 @@
 //   ks_count, ks_scan, ks_scatter   the plan: per sequence, a counting sort
 //              of the (query, slot) entries of the selection (and each
 //              query's tail) by block: the block's list of queries, cut into
-//              work items of up to kKsItemMax queries.
+//              work items of up to kKsItemMax queries.  Where a sequence has
+//              at most kScanThreads candidate blocks, ks_scan_scatter does
+//              the last two steps in one launch.
 //   ks_attn    one workgroup per (item, KV head): the block's K and V rows go
 //              to LDS once; the item's queries run through it 64 (query,
 //              head) rows at a time as dense bf16 MFMA tiles, S^T = K Q^T
@@ -270,6 +272,78 @@ __global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
     const int t = ta + e / K1, slot = e - (e / K1) * K1;
     const int j = entry_block(g, a, sel, nblk, past + (t - cu0), t, slot);
     if (j >= 0) a.list[atomicAdd(&pos_lds[j], 1)] = pack_entry(t, slot);
+  }
+}
+
+// Plan, steps 2 and 3 in one launch, for sequences of at most kScanThreads
+// candidate blocks (+ the tail): grid (query group, sequence), one thread per
+// block.  Each workgroup reads its sequence's whole histogram (one column
+// per thread, kGroup entries deep) and derives its own list positions from
+// it: the block's first position from the sums of every group, then the
+// entries of the block from the groups before this one.  The group-0
+// workgroup also cuts the work items, in the same order and form as
+// ks_scan_kernel.  Without the one-workgroup scan between them, counting and
+// scattering are two launches instead of three.
+__global__ __launch_bounds__(kScanThreads) void ks_scan_scatter_kernel(
+    Geo g, KsArgs a, const int32_t* __restrict__ sel, const int32_t* __restrict__ nblk) {
+  extern __shared__ int32_t pos_lds[];
+  __shared__ int sh[kScanThreads / 64];
+  const int gi = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const SeqRange sr = seq_range(g, a, b);
+  const int ta = min(sr.t0 + gi * kGroup, sr.t1), tb = min(sr.t1, ta + kGroup);
+  if (gi > 0 && ta >= tb) return;  // (the whole workgroup: no queries in this group)
+  const int NB1 = a.nb1, ng = a.ng, j = tid;
+  const int32_t* rows = a.hist + (int64_t)b * ng * NB1;
+  // c[r]: entries of block j from the groups of range r; before: from the
+  // groups ahead of this one
+  int c[kMaxRanges], before = 0;
+#pragma unroll
+  for (int r = 0; r < kMaxRanges; ++r) c[r] = 0;
+  if (j < NB1) {
+    constexpr int GB = 32;  // group rows per batch of loads
+#pragma unroll
+    for (int g0 = 0; g0 < kMaxRanges * kRangeGroups; g0 += GB) {
+      if (g0 >= ng) break;
+      int v[GB];
+#pragma unroll
+      for (int x = 0; x < GB; ++x) v[x] = (g0 + x < ng) ? rows[(int64_t)(g0 + x) * NB1 + j] : 0;
+#pragma unroll
+      for (int x = 0; x < GB; ++x) {
+        c[(g0 + x) / kRangeGroups] += v[x];
+        before += (g0 + x < gi) ? v[x] : 0;
+      }
+    }
+  }
+  int tot = 0;
+#pragma unroll
+  for (int r = 0; r < kMaxRanges; ++r) tot += c[r];
+  int total_ents;
+  const int ent_before = scan_excl(tot, &total_ents, sh);
+  const int o = (sr.t0 - a.t_lo) * a.k1 + ent_before;  // block j's first list position
+  if (j < NB1) pos_lds[j] = o + before;
+  if (gi == 0) {
+    const int n_ranges = (ng + kRangeGroups - 1) / kRangeGroups;
+    const int base_next = item_base(a, b + 1, sr.t1 - a.t_lo);
+    int it0 = item_base(a, b, sr.t0 - a.t_lo), pos = o;
+#pragma unroll
+    for (int r = 0; r < kMaxRanges; ++r) {
+      if (r >= n_ranges) break;  // uniform: every thread reaches the same scans
+      int total_items;
+      int it = it0 + scan_excl((c[r] + a.item_tokens - 1) / a.item_tokens, &total_items, sh);
+      for (int x = 0; x < c[r]; x += a.item_tokens, ++it)
+        a.items[it] = make_int4(pos + x, j, min(a.item_tokens, c[r] - x), b);
+      pos += c[r];
+      it0 += total_items;
+    }
+    for (int x = it0 + tid; x < base_next; x += kScanThreads) a.items[x] = make_int4(0, 0, 0, b);
+    if (ta >= tb) return;  // (the whole workgroup: a sequence without queries here)
+  }
+  __syncthreads();
+  const int past = g.past_len[b], cu0 = g.cu_q[b], K1 = a.k1;
+  for (int e = tid; e < (tb - ta) * K1; e += kScanThreads) {
+    const int t = ta + e / K1, slot = e - (e / K1) * K1;
+    const int jj = entry_block(g, a, sel, nblk, past + (t - cu0), t, slot);
+    if (jj >= 0) a.list[atomicAdd(&pos_lds[jj], 1)] = pack_entry(t, slot);
   }
 }
 
@@ -758,11 +832,14 @@ hipError_t launch_attend_ks(const Geo& g, const KsWork& w, const void* q, const 
       ks_rotate_q_kernel<<<(int)(((int64_t)(a.t_hi - a.t_lo) * g.Hq + 15) / 16), 256, 0, st>>>(
           g, a, static_cast<const uint16_t*>(q));
     ks_count_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
-    if (a.nb1 <= kScanThreads) ks_scan_kernel<1><<<g.B, kScanThreads, 0, st>>>(g, a);
-    else if (a.nb1 <= 2 * kScanThreads) ks_scan_kernel<2><<<g.B, kScanThreads, 0, st>>>(g, a);
-    else if (a.nb1 <= 4 * kScanThreads) ks_scan_kernel<4><<<g.B, kScanThreads, 0, st>>>(g, a);
-    else ks_scan_kernel<8><<<g.B, kScanThreads, 0, st>>>(g, a);
-    ks_scatter_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
+    if (a.nb1 <= kScanThreads) {
+      ks_scan_scatter_kernel<<<dim3(a.ng, g.B), kScanThreads, lds, st>>>(g, a, sel, n_blocks);
+    } else {
+      if (a.nb1 <= 2 * kScanThreads) ks_scan_kernel<2><<<g.B, kScanThreads, 0, st>>>(g, a);
+      else if (a.nb1 <= 4 * kScanThreads) ks_scan_kernel<4><<<g.B, kScanThreads, 0, st>>>(g, a);
+      else ks_scan_kernel<8><<<g.B, kScanThreads, 0, st>>>(g, a);
+      ks_scatter_kernel<<<dim3(a.ng, g.B), 256, lds, st>>>(g, a, sel, n_blocks);
+    }
     switch (g.G) {
       case 1: ks_launch_g<1>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
       case 2: ks_launch_g<2>(g, a, n_items, q, k_cache, v_cache, sel, n_blocks, gate, out, st); break;
