@@ -199,6 +199,28 @@ def test_prefill_selection_ties_at_the_boundary():
     _full(case)
 
 
+@pytest.mark.parametrize("extra", [0, 40000, 140000])
+def test_prefill_selection_tie_classes_every_select_path(extra):
+    """Indexer keys that repeat one of three patterns block by block, so that
+    a query's scores take at most three values and its k-th score is shared
+    by many blocks: inside that class the selection is the tie rule alone.
+    Cache capacities of 4.1K, 44K and 144K tokens make the score rows 64,
+    689 and 2252 candidates wide, which puts them on each of the three
+    selection kernels (a wave per query; a workgroup per query with the keys
+    in registers; the keys in memory) and the plan on both of its forms."""
+    case = workloads.make_case("chunked_prefill_32k_bf16", prefill_len=4096 + 37, chunk=1024)
+    r = case.spec.block_size
+    rng = np.random.default_rng(7)
+    for b in range(case.spec.n_seqs):
+        kI = workloads.as_f32(case.kI[b]).copy()
+        pats = rng.integers(-2, 3, size=(3, kI.shape[1])).astype(np.float32) * 0.25
+        cls = rng.integers(0, 3, size=kI.shape[0] // r)
+        for blk, c in enumerate(cls):
+            kI[blk * r:(blk + 1) * r] = pats[c]
+        case.kI[b] = workloads.bf16_bits(kI)
+    _full(case, extra_steps=extra)
+
+
 # ----------------------------------------------------------------- the pages' case
 def test_pages_worked_count_released_config():
     """kv_len 3002, ratio 4, budget 2048: 512 of 750 blocks and 2050 keys
