@@ -221,6 +221,24 @@ def test_prefill_selection_tie_classes_every_select_path(extra):
     _full(case, extra_steps=extra)
 
 
+def test_decode_selection_tie_classes():
+    """The tie classes of the prefill test above through the decode path,
+    where every attention workgroup makes the selection itself: ragged paged
+    contexts with up to 140 candidate blocks, k = 64."""
+    case = workloads.make_case("ragged_paged_decode_128k_bf16", n_seqs=9, ctx_range=(70, 9000),
+                               steps=3)
+    r = case.spec.block_size
+    rng = np.random.default_rng(11)
+    for b in range(case.spec.n_seqs):
+        kI = workloads.as_f32(case.kI[b]).copy()
+        pats = rng.integers(-2, 3, size=(3, kI.shape[1])).astype(np.float32) * 0.25
+        cls = rng.integers(0, 3, size=kI.shape[0] // r)
+        for blk, c in enumerate(cls):
+            kI[blk * r:(blk + 1) * r] = pats[c]
+        case.kI[b] = workloads.bf16_bits(kI)
+    _full(case, layout="paged")
+
+
 # ----------------------------------------------------------------- the pages' case
 def test_pages_worked_count_released_config():
     """kv_len 3002, ratio 4, budget 2048: 512 of 750 blocks and 2050 keys
