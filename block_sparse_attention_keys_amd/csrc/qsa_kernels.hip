@@ -888,9 +888,10 @@ __global__ __launch_bounds__(256) void select_kernel(Geo g, const float* __restr
 // passes and the same tie rule as block_radix_topk, on a histogram of the
 // wave's own in LDS: no workgroup barrier anywhere, so the calls with many
 // queries (prefill) keep four times as many selections in flight per CU as
-// with a workgroup per query.  A wave's LDS operations complete in the order
-// it issues them; the wavefront-scope fences keep the compiler from moving
-// them across the phase boundaries and wait for them to complete.
+// with a workgroup per query.  The LDS performs one wave's operations in the
+// order the wave issues them, so nothing has to wait between clearing the
+// histogram, counting into it and reading it back; the wavefront-scope fence
+// and wave barrier only keep the compiler from reordering those phases.
 constexpr int kSelectWaveBlocks = 512;
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

@@ -277,9 +277,9 @@ __global__ __launch_bounds__(256) void ks_scatter_kernel(Geo g, KsArgs a,
 
 // Plan, steps 2 and 3 in one launch, for sequences of at most kScanThreads
 // candidate blocks (+ the tail): grid (query group, sequence), one thread per
-// block.  Each workgroup reads its sequence's whole histogram (one column
-// per thread, kGroup entries deep) and derives its own list positions from
-// it: the block's first position from the sums of every group, then the
+// block.  Each workgroup reads its sequence's whole histogram (each thread
+// its block's column, one entry per group) and derives its own list
+// positions from it: the block's first position from the sums of every group, then the
 // entries of the block from the groups before this one.  The group-0
 // workgroup also cuts the work items, in the same order and form as
 // ks_scan_kernel.  Without the one-workgroup scan between them, counting and
